@@ -1,0 +1,180 @@
+/*
+ * loki.h -- C ABI of the Loki sparse decode-attention library for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * Method: "Loki: Low-Rank Keys for Efficient Sparse Attention" (Singhania,
+ * Singh, He, Feizi, Bhatele; NeurIPS 2024).  Keys are cached in a PCA basis
+ * calibrated offline; each decode step rotates the query into that basis,
+ * scores every cached token with the leading d principal components only,
+ * keeps the top k tokens per (batch, query head) and runs exact softmax
+ * attention with the full-dimensional keys over those k tokens.  Sources:
+ *   [A]  briefgpt.xyz keyword page "loki" -- the paper's abstract: tokens are
+ *        ranked and selected by attention scores computed in low-dimensional
+ *        space;
+ *   [T]  deep-diver.github.io NeurIPS-2024 poster page, "TL;DR": full-
+ *        dimensional scores only for the selected tokens;
+ *   [F1] same page, "Visual Insights", Figure 1 (right): offline PCA of the
+ *        keys, approximate scores in the low-dimensional space, top-k, final
+ *        scores with the full-dimensional keys;
+ *   [C]  same page, "In-depth insights", "Loki's Computational Cost": the
+ *        KV-cache append is part of each step;
+ *   [TB] same page, "More on tables", first table: k_f is the fraction of keys
+ *        kept, d_f the fraction of the key dimensions used for scoring.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, at least
+ *     16-byte aligned; the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; the call returns after enqueueing.
+ *   - Arguments are validated before anything is enqueued: on any error
+ *     nothing is launched and no output is written.  Return value 0 = OK,
+ *     negative = loki_status; loki_last_error() gives a detail string
+ *     (thread-local).  A launch failure reported by the HIP runtime returns
+ *     LOKI_EHIP.
+ *   - Calls that share a workspace must not overlap in time.
+ *
+ * Layouts (element = the storage dtype of loki_desc.dtype)
+ *   q        [B, Hq, D]
+ *   V cache  [B, Hkv, S_cap, D] row-major
+ *   K cache  rotated keys (k . P) in the split-panel layout: per (b, kv) one
+ *            block of S_cap*D elements, first the leading dp coordinates of
+ *            every token ([S_cap, dp], token-major), then the remaining D-dp
+ *            coordinates ([S_cap, D-dp]).  Same size as a row-major cache.
+ *            Written only through loki_pack_kcache, loki_append and
+ *            loki_decode_append.
+ *   P        [Hkv, D, D] fp32 row-major; column j is the j-th principal
+ *            direction (descending variance), so k_rot = k . P.  Query head h
+ *            uses P[h / (Hq/Hkv)].
+ *   qr       [B, Hq, D] fp32, scores [B, Hq, S] fp32, idx [B, Hq, k] int32,
+ *   out      [B, Hq, D] fp32.
+ */
+#ifndef LOKI_H
+#define LOKI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOKI_OK = 0,
+  LOKI_EINVAL = -1,       /* argument outside its documented domain, null or misaligned pointer */
+  LOKI_EUNSUPPORTED = -2, /* valid but not built: head_dim, panel width, GQA group size */
+  LOKI_EWORKSPACE = -3,   /* workspace smaller than loki_workspace_bytes() */
+  LOKI_EHIP = -4          /* the HIP runtime refused a launch */
+} loki_status;
+
+typedef enum { LOKI_F32 = 0, LOKI_F16 = 1, LOKI_BF16 = 2 } loki_dtype;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq/Hkv in 1..16 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t seq_len;      /* S: tokens attended, 1 <= S <= seq_capacity */
+  int32_t seq_capacity; /* S_cap: rows allocated per (b, kv) in both caches */
+  int32_t panel_dim;    /* dp: leading rotated coordinates stored as the scoring
+                           panel; a power of two, 16 <= dp*elem_bytes, dp <= D.
+                           Scoring is fastest with d <= dp, the final attention
+                           with d == dp. */
+  int32_t dtype;        /* loki_dtype of q, K cache, V cache, k_new, v_new */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(D) */
+} loki_desc;
+
+/* Human-readable name of a status code; never NULL. */
+const char* loki_strerror(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* loki_last_error(void);
+
+/* Number of elements of the K cache (= B*Hkv*S_cap*D) for `desc`. */
+int loki_kcache_elems(const loki_desc* desc, size_t* n_elems);
+
+/* Bytes of workspace loki_decode / loki_decode_append need for (d, k). */
+int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes);
+
+/*
+ * Cache layout conversion.  krot_rows [B, Hkv, n_tokens, D] row-major rotated
+ * keys <-> the first n_tokens rows of every (b, kv) block of the K cache.
+ * n_tokens in [0, S_cap].  Pure data movement.
+ */
+int loki_pack_kcache(const void* krot_rows, int32_t n_tokens, void* kcache,
+                     const loki_desc* desc, void* stream);
+int loki_unpack_kcache(const void* kcache, int32_t n_tokens, void* krot_rows,
+                       const loki_desc* desc, void* stream);
+
+/*
+ * Append one token per (b, kv) at row `pos` (0 <= pos < S_cap) [C], [F1]:
+ * K cache row pos := round_to_dtype(k_new . P[kv]) (fp32 product, rounded to
+ * nearest even), V cache row pos := v_new (copied).  k_new, v_new [B, Hkv, D].
+ */
+int loki_append(const void* k_new, const void* v_new, const float* P, void* kcache,
+                void* vcache, int32_t pos, const loki_desc* desc, void* stream);
+
+/* Query rotation [F1]: qr[b,h,:] = q[b,h,:] . P[h / (Hq/Hkv)] in fp32. */
+int loki_rotate_query(const void* q, const float* P, float* qr, const loki_desc* desc,
+                      void* stream);
+
+/*
+ * Approximate scores [A], [F1], [TB]:
+ * scores[b,h,t] = sum_{j<d} qr[b,h,j] * krot[b,kv,t,j] for t < S, 1 <= d <= D.
+ * No scaling.
+ */
+int loki_score(const float* qr, const void* kcache, int d, float* scores,
+               const loki_desc* desc, void* stream);
+
+/*
+ * Top-k selection [A], [T], [TB]: idx[b,h,:] = the k tokens ranked first by
+ * (score descending, token ascending), listed in ascending token order;
+ * -0 ranks as +0.  1 <= k <= S.  Scores must not be NaN.
+ */
+int loki_topk(const float* scores, int k, int32_t* idx, const loki_desc* desc, void* stream);
+
+/*
+ * Exact attention over given token sets [T], [F1]:
+ * z_t = scale * sum_{j<D} qr[b,h,j] krot[b,kv,t,j] for t in idx[b,h,:],
+ * out[b,h,:] = sum_t softmax(z)_t V[b,kv,t,:].  Entries of idx outside
+ * [0, S) contribute zero weight (all of them outside -> NaN row).
+ * Needs loki_workspace_bytes(desc, D, k) bytes of workspace.
+ */
+int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
+                int k, float* out, const loki_desc* desc, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * One full Loki decode step [A], [T], [F1]: rotate q, score all S tokens
+ * with the leading d coordinates, select the top k per (b, h), exact softmax
+ * attention over them.  1 <= d <= D, 1 <= k <= S.  idx_out (nullable)
+ * receives the selected sets [B, Hq, k] in ascending order.
+ */
+int loki_decode(const void* q, const void* kcache, const void* vcache, const float* P, int d,
+                int k, float* out, int32_t* idx_out, const loki_desc* desc, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Append then decode [C], [F1]: appends (k_new, v_new) at row pos = S-1 as
+ * loki_append does, then runs loki_decode over the S tokens (the new one
+ * included).  The append shares the query-rotation launch.
+ */
+int loki_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
+                       void* vcache, const float* P, int d, int k, float* out,
+                       int32_t* idx_out, const loki_desc* desc, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic hook (no method content): while set, every loki_decode /
+ * loki_decode_append call made by THIS thread records events[0..4] (each a
+ * hipEvent_t created by the caller) on its stream: before the query rotation,
+ * before the scoring, before the top-k, before the attention, and after the
+ * attention.  n_events = 0 clears the hook; any other count but 5 is
+ * LOKI_EINVAL.  The events stay owned by the caller.
+ */
+int loki_profile_events(void* const* events, int n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOKI_H */

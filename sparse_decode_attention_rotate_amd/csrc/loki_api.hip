@@ -1,0 +1,401 @@
+// extern "C" entry points of libloki: argument validation, workspace layout,
+// and the launch sequence of one decode step.  See include/loki.h for the
+// contract of each call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "loki.h"
+#include "loki_internal.h"
+
+using namespace loki;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Diagnostic hook: events recorded before each phase of a decode step and
+// after the last one (loki_profile_events).
+thread_local hipEvent_t g_prof_events[5];
+thread_local int g_prof_n = 0;
+
+hipError_t mark(int i, hipStream_t st) {
+  if (g_prof_n == 5) return hipEventRecord(g_prof_events[i], st);
+  return hipSuccess;
+}
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LOKI_OK;
+  return fail(LOKI_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == LOKI_F32 ? 4 : 2; }
+
+#define REQUIRE_PTR(p)                                                             \
+  do {                                                                             \
+    if ((p) == nullptr) return fail(LOKI_EINVAL, "%s is NULL", #p);                \
+    if (!aligned16(p)) return fail(LOKI_EINVAL, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+
+int check_desc(const loki_desc* d, Shape* sh) {
+  if (!d) return fail(LOKI_EINVAL, "desc is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(LOKI_EINVAL, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(LOKI_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                d->n_q_heads, d->n_kv_heads);
+  const int g = d->n_q_heads / d->n_kv_heads;
+  if (g > 16) return fail(LOKI_EUNSUPPORTED, "query heads per KV head (%d) above 16", g);
+  if (d->dtype != LOKI_F32 && d->dtype != LOKI_F16 && d->dtype != LOKI_BF16)
+    return fail(LOKI_EINVAL, "dtype %d is not a loki_dtype", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(LOKI_EUNSUPPORTED, "head_dim %d (built: 64, 128)", d->head_dim);
+  if (d->seq_len < 1 || d->seq_capacity < d->seq_len || d->seq_capacity > (1 << 30))
+    return fail(LOKI_EINVAL, "need 1 <= seq_len (%d) <= seq_capacity (%d) <= 2^30",
+                d->seq_len, d->seq_capacity);
+  const int dp = d->panel_dim, eb = elem_bytes(d->dtype);
+  if (dp < 1 || dp > d->head_dim || (dp & (dp - 1)) != 0 || dp * eb < 16)
+    return fail(LOKI_EINVAL,
+                "panel_dim %d must be a power of two <= head_dim with panel_dim*elem >= 16", dp);
+  sh->B = d->batch;
+  sh->Hq = d->n_q_heads;
+  sh->Hkv = d->n_kv_heads;
+  sh->g = g;
+  sh->D = d->head_dim;
+  sh->S = d->seq_len;
+  sh->S_cap = d->seq_capacity;
+  sh->dp = dp;
+  sh->dtype = d->dtype;
+  sh->kl.head_elems = (size_t)d->seq_capacity * d->head_dim;
+  sh->kl.rest_off = (size_t)d->seq_capacity * dp;
+  sh->kl.dp = dp;
+  sh->kl.rest = d->head_dim - dp;
+  return LOKI_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t qr, scores, idx, sel, part, total;
+  int nsplit;
+};
+
+WsLayout ws_layout(const Shape& sh, int k) {
+  WsLayout w;
+  const size_t units = (size_t)sh.B * sh.Hq;
+  w.nsplit = (k + kAttendChunk - 1) / kAttendChunk;
+  size_t off = 0;
+  w.qr = off;
+  off += align256(units * sh.D * 4);
+  w.scores = off;
+  off += align256(units * sh.S * 4);
+  w.idx = off;
+  off += align256(units * (size_t)k * 4);
+  w.sel = off;
+  off += align256(units * (size_t)k * 4);
+  w.part = off;
+  off += w.nsplit > 1 ? align256(units * w.nsplit * (size_t)(sh.D + 2) * 4) : 0;
+  w.total = off;
+  return w;
+}
+
+float scale_log2(const loki_desc* d) {
+  const float s = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return s * 1.4426950408889634f;  // log2(e)
+}
+
+int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                const float* P, int d, int k, float* out, int32_t* idx_out,
+                const loki_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
+                bool append) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(vcache);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(workspace);
+  if (append) {
+    REQUIRE_PTR(k_new);
+    REQUIRE_PTR(v_new);
+  }
+  if (idx_out && !aligned16(idx_out)) return fail(LOKI_EINVAL, "idx_out is not 16-byte aligned");
+  if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
+  if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
+  const WsLayout w = ws_layout(sh, k);
+  if (workspace_bytes < w.total)
+    return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  float* qr = reinterpret_cast<float*>(ws + w.qr);
+  float* scores = reinterpret_cast<float*>(ws + w.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + w.idx);
+  const bool split = (d == sh.dp);
+  float* sel = split ? reinterpret_cast<float*>(ws + w.sel) : nullptr;
+
+  ProjectParams pp{};
+  pp.q = q;
+  pp.k_new = append ? k_new : nullptr;
+  pp.v_new = append ? v_new : nullptr;
+  pp.P = P;
+  pp.qr = qr;
+  pp.kcache = kcache;
+  pp.vcache = vcache;
+  pp.pos = sh.S - 1;
+  pp.sh = sh;
+  if ((rc = hip_status(mark(0, st), "event"))) return rc;
+  if ((rc = hip_status(launch_project(pp, st), "project"))) return rc;
+  if ((rc = hip_status(mark(1, st), "event"))) return rc;
+
+  ScoreParams sp{};
+  sp.qr = qr;
+  sp.kcache = kcache;
+  sp.scores = scores;
+  sp.d = d;
+  sp.sh = sh;
+  if ((rc = hip_status(launch_score(sp, st), "score"))) return rc;
+  if ((rc = hip_status(mark(2, st), "event"))) return rc;
+
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.idx = idx;
+  tp.sel_scores = sel;
+  tp.S = sh.S;
+  tp.k = k;
+  if ((rc = hip_status(launch_topk(tp, sh.B * sh.Hq, st), "topk"))) return rc;
+  if ((rc = hip_status(mark(3, st), "event"))) return rc;
+
+  AttendParams ap{};
+  ap.qr = qr;
+  ap.kcache = kcache;
+  ap.vcache = vcache;
+  ap.idx = idx;
+  ap.sel_scores = sel;
+  ap.out = out;
+  ap.part = reinterpret_cast<float*>(ws + w.part);
+  ap.k = k;
+  ap.d = d;
+  ap.nsplit = w.nsplit;
+  ap.kc = kAttendChunk;
+  ap.scale_log2 = scale_log2(desc);
+  ap.sh = sh;
+  if ((rc = hip_status(launch_attend(ap, st), "attend"))) return rc;
+  return hip_status(mark(4, st), "event");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* loki_strerror(int status) {
+  switch (status) {
+    case LOKI_OK: return "ok";
+    case LOKI_EINVAL: return "invalid argument";
+    case LOKI_EUNSUPPORTED: return "unsupported configuration";
+    case LOKI_EWORKSPACE: return "workspace too small";
+    case LOKI_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* loki_last_error(void) { return g_last_error.c_str(); }
+
+int loki_profile_events(void* const* events, int n_events) {
+  if (n_events == 0) {
+    g_prof_n = 0;
+    return LOKI_OK;
+  }
+  if (n_events != 5 || !events) return fail(LOKI_EINVAL, "need 5 events (got %d)", n_events);
+  for (int i = 0; i < 5; i++) {
+    if (!events[i]) return fail(LOKI_EINVAL, "event %d is NULL", i);
+    g_prof_events[i] = (hipEvent_t)events[i];
+  }
+  g_prof_n = 5;
+  return LOKI_OK;
+}
+
+int loki_kcache_elems(const loki_desc* desc, size_t* n_elems) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  if (!n_elems) return fail(LOKI_EINVAL, "n_elems is NULL");
+  *n_elems = (size_t)sh.B * sh.Hkv * sh.kl.head_elems;
+  return LOKI_OK;
+}
+
+int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  if (!bytes) return fail(LOKI_EINVAL, "bytes is NULL");
+  if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
+  if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
+  *bytes = ws_layout(sh, k).total;
+  return LOKI_OK;
+}
+
+static int layout_impl(const void* src, void* dst, int32_t n_tokens, const loki_desc* desc,
+                       void* stream, int to_cache) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(dst);
+  if (n_tokens < 0 || n_tokens > sh.S_cap)
+    return fail(LOKI_EINVAL, "n_tokens = %d outside [0, %d]", n_tokens, sh.S_cap);
+  LayoutParams p{};
+  p.src = src;
+  p.dst = dst;
+  p.n_tokens = n_tokens;
+  p.to_cache = to_cache;
+  p.sh = sh;
+  return hip_status(launch_layout(p, (hipStream_t)stream), "layout");
+}
+
+int loki_pack_kcache(const void* krot_rows, int32_t n_tokens, void* kcache,
+                     const loki_desc* desc, void* stream) {
+  return layout_impl(krot_rows, kcache, n_tokens, desc, stream, 1);
+}
+
+int loki_unpack_kcache(const void* kcache, int32_t n_tokens, void* krot_rows,
+                       const loki_desc* desc, void* stream) {
+  return layout_impl(kcache, krot_rows, n_tokens, desc, stream, 0);
+}
+
+int loki_append(const void* k_new, const void* v_new, const float* P, void* kcache,
+                void* vcache, int32_t pos, const loki_desc* desc, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(v_new);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(vcache);
+  if (pos < 0 || pos >= sh.S_cap) return fail(LOKI_EINVAL, "pos = %d outside [0, %d)", pos, sh.S_cap);
+  ProjectParams pp{};
+  pp.k_new = k_new;
+  pp.v_new = v_new;
+  pp.P = P;
+  pp.kcache = kcache;
+  pp.vcache = vcache;
+  pp.pos = pos;
+  pp.sh = sh;
+  return hip_status(launch_project(pp, (hipStream_t)stream), "append");
+}
+
+int loki_rotate_query(const void* q, const float* P, float* qr, const loki_desc* desc,
+                      void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(qr);
+  ProjectParams pp{};
+  pp.q = q;
+  pp.P = P;
+  pp.qr = qr;
+  pp.sh = sh;
+  return hip_status(launch_project(pp, (hipStream_t)stream), "rotate_query");
+}
+
+int loki_score(const float* qr, const void* kcache, int d, float* scores, const loki_desc* desc,
+               void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(qr);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(scores);
+  if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
+  ScoreParams sp{};
+  sp.qr = qr;
+  sp.kcache = kcache;
+  sp.scores = scores;
+  sp.d = d;
+  sp.sh = sh;
+  return hip_status(launch_score(sp, (hipStream_t)stream), "score");
+}
+
+int loki_topk(const float* scores, int k, int32_t* idx, const loki_desc* desc, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(idx);
+  if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.idx = idx;
+  tp.S = sh.S;
+  tp.k = k;
+  return hip_status(launch_topk(tp, sh.B * sh.Hq, (hipStream_t)stream), "topk");
+}
+
+int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
+                int k, float* out, const loki_desc* desc, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(qr);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(vcache);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(workspace);
+  if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
+  const WsLayout w = ws_layout(sh, k);
+  if (workspace_bytes < w.total)
+    return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+  AttendParams ap{};
+  ap.qr = qr;
+  ap.kcache = kcache;
+  ap.vcache = vcache;
+  ap.idx = idx;
+  ap.out = out;
+  ap.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part);
+  ap.k = k;
+  ap.d = sh.D;
+  ap.nsplit = w.nsplit;
+  ap.kc = kAttendChunk;
+  ap.scale_log2 = scale_log2(desc);
+  ap.sh = sh;
+  return hip_status(launch_attend(ap, (hipStream_t)stream), "attend");
+}
+
+int loki_decode(const void* q, const void* kcache, const void* vcache, const float* P, int d,
+                int k, float* out, int32_t* idx_out, const loki_desc* desc, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, nullptr, const_cast<void*>(kcache), const_cast<void*>(vcache),
+                     P, d, k, out, idx_out, desc, workspace, workspace_bytes, stream, false);
+}
+
+int loki_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
+                       void* vcache, const float* P, int d, int k, float* out,
+                       int32_t* idx_out, const loki_desc* desc, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_new, v_new, kcache, vcache, P, d, k, out, idx_out, desc, workspace,
+                     workspace_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Device-side helpers shared by the Loki kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace loki {
+
+enum Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <int DT> struct Elem;
+template <> struct Elem<F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;  // elements in one 16-byte load
+};
+template <> struct Elem<F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+};
+template <> struct Elem<BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+};
+
+// ---------------------------------------------------------------- dtype I/O
+
+// One 16-byte vector -> kPerVec floats (exact widening).
+template <int DT> __device__ __forceinline__ void unpack16(u32x4 v, float* f);
+
+template <> __device__ __forceinline__ void unpack16<F32>(u32x4 v, float* f) {
+  f[0] = __uint_as_float(v.x);
+  f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z);
+  f[3] = __uint_as_float(v.w);
+}
+
+template <> __device__ __forceinline__ void unpack16<F16>(u32x4 v, float* f) {
+  f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+  for (int i = 0; i < 8; i++) f[i] = (float)h[i];
+}
+
+template <> __device__ __forceinline__ void unpack16<BF16>(u32x4 v, float* f) {
+  // element 2w sits in the low half of dword w (little endian)
+  unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <int DT> __device__ __forceinline__ float load_elem(const void* base, size_t i);
+template <> __device__ __forceinline__ float load_elem<F32>(const void* base, size_t i) {
+  return static_cast<const float*>(base)[i];
+}
+template <> __device__ __forceinline__ float load_elem<F16>(const void* base, size_t i) {
+  return (float)static_cast<const _Float16*>(base)[i];
+}
+template <> __device__ __forceinline__ float load_elem<BF16>(const void* base, size_t i) {
+  return __uint_as_float((unsigned)static_cast<const unsigned short*>(base)[i] << 16);
+}
+
+// fp32 -> storage dtype, round to nearest, ties to even.
+template <int DT> __device__ __forceinline__ void store_elem(void* base, size_t i, float x);
+template <> __device__ __forceinline__ void store_elem<F32>(void* base, size_t i, float x) {
+  static_cast<float*>(base)[i] = x;
+}
+template <> __device__ __forceinline__ void store_elem<F16>(void* base, size_t i, float x) {
+  static_cast<_Float16*>(base)[i] = (_Float16)x;
+}
+template <> __device__ __forceinline__ void store_elem<BF16>(void* base, size_t i, float x) {
+  unsigned u = __float_as_uint(x);
+  unsigned short r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    r = (unsigned short)((u >> 16) | 0x40u);  // quiet NaN
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);            // round half to even on bit 16
+    r = (unsigned short)(u >> 16);
+  }
+  static_cast<unsigned short*>(base)[i] = r;
+}
+
+// Raw element copy (no conversion), for moving stored rows.
+template <int DT> __device__ __forceinline__ void copy_elem(void* dst, size_t di, const void* src,
+                                                            size_t si) {
+  if constexpr (Elem<DT>::kBytes == 4)
+    static_cast<unsigned*>(dst)[di] = static_cast<const unsigned*>(src)[si];
+  else
+    static_cast<unsigned short*>(dst)[di] = static_cast<const unsigned short*>(src)[si];
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// DPP move within a row of 16 lanes (ctrl is the gfx9 DPP control word).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of L lanes; every lane of a group gets the group sum.
+template <int L> __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (L >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// DPP shift within a row with zero fill for lanes that have no source.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ unsigned dpp_shift_u(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xf, false);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, DPP only.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
+  x += dpp_shift_u<0x111>(x);          // row_shr:1
+  x += dpp_shift_u<0x112>(x);          // row_shr:2
+  x += dpp_shift_u<0x114>(x);          // row_shr:4
+  x += dpp_shift_u<0x118>(x);          // row_shr:8   (prefix within each row of 16)
+  x += dpp_shift_u<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
+  x += dpp_shift_u<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Number of set bits of a wave ballot below this lane.
+__device__ __forceinline__ int lane_rank(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+// ---------------------------------------------------------------- K cache layout
+//
+// Split-panel rotated key cache.  Per (batch, KV head) one block of S_cap*D
+// elements: first the leading `dp` rotated coordinates of every token
+// (token-major, S_cap x dp), then the remaining D-dp coordinates
+// (S_cap x (D-dp)).  Scoring streams the first part contiguously; the final
+// attention reads the second part of the selected rows.
+struct KLayout {
+  size_t head_elems;  // S_cap * D
+  size_t rest_off;    // S_cap * dp
+  int dp;             // panel width
+  int rest;           // D - dp
+
+  __host__ __device__ size_t at(size_t head, size_t t, int j) const {
+    return head * head_elems +
+           (j < dp ? t * (size_t)dp + j : rest_off + t * (size_t)rest + (size_t)(j - dp));
+  }
+};
+
+}  // namespace loki

@@ -1,0 +1,76 @@
+// Kernel parameter blocks and launcher declarations (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "loki_common.h"
+
+namespace loki {
+
+struct Shape {
+  int B, Hq, Hkv, g, D, S, S_cap, dp, dtype;
+  KLayout kl;
+};
+
+struct ProjectParams {
+  const void* q;      // [B,Hq,D] storage dtype (nullable: no query rotation)
+  const void* k_new;  // [B,Hkv,D] (nullable: no append)
+  const void* v_new;  // [B,Hkv,D]
+  const float* P;     // [Hkv,D,D]
+  float* qr;          // [B,Hq,D] fp32
+  void* kcache;
+  void* vcache;
+  int pos;            // append row
+  int bb;             // batch rows per workgroup
+  Shape sh;
+};
+
+struct ScoreParams {
+  const float* qr;     // [B,Hq,D]
+  const void* kcache;
+  float* scores;       // [B,Hq,S]
+  int d;
+  int n_tiles;         // tiles per (b, kv)
+  Shape sh;
+};
+
+struct TopkParams {
+  const float* scores;  // [B*Hq, S]
+  int32_t* idx;         // [B*Hq, k] ascending
+  float* sel_scores;    // [B*Hq, k] nullable: low-dim score of each selected token
+  int S, k;
+};
+
+struct AttendParams {
+  const float* qr;          // [B,Hq,D]
+  const void* kcache;
+  const void* vcache;
+  const int32_t* idx;       // [B*Hq, k]
+  const float* sel_scores;  // [B*Hq, k] low-dim partial logits (split variant) or null
+  float* out;               // [B,Hq,D] fp32 (written when nsplit == 1 or by combine)
+  float* part;              // [B*Hq, nsplit, D+2] partial (m, l, acc)
+  int k, d, nsplit, kc;
+  float scale_log2;         // softmax scale * log2(e)
+  Shape sh;
+};
+
+struct LayoutParams {
+  const void* src;
+  void* dst;
+  int n_tokens;
+  int to_cache;  // 1: row-major -> cache layout, 0: cache -> row-major
+  Shape sh;
+};
+
+hipError_t launch_project(const ProjectParams& p, hipStream_t st);
+hipError_t launch_score(const ScoreParams& p, hipStream_t st);
+hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st);
+hipError_t launch_attend(const AttendParams& p, hipStream_t st);
+hipError_t launch_layout(const LayoutParams& p, hipStream_t st);
+
+// Rows of the selected set processed by one attention workgroup.
+constexpr int kAttendChunk = 128;
+
+}  // namespace loki

@@ -1,0 +1,144 @@
+// Approximate (low-dimensional) attention scores of every cached token.
+//
+// Loki (briefgpt.xyz abstract; poster page "Visual Insights", Figure 1 right):
+// tokens are ranked by attention scores computed from the leading principal
+// components only.  s[b,h,t] = sum_{j<d} qr[b,h,j] * krot[b,kv,t,j].
+//
+// Fast path (d <= dp): the leading dp coordinates of all tokens of one
+// (batch, KV head) are one contiguous panel, so a workgroup streams a tile of
+// it with 16-byte loads, LPT lanes per token (LPT = dp*elem/16), every lane
+// holding the matching fp32 slice of qr for each query head of the KV group;
+// the LPT partial dot products are summed with DPP.  One pass over the panel
+// serves all g query heads of a GQA group.
+#include "loki_internal.h"
+
+namespace loki {
+
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreIters = 16;  // 16-byte loads in flight per lane
+
+template <int DT, int LPT, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams p) {
+  constexpr int E = Elem<DT>::kPerVec;
+  constexpr int TPP = kScoreThreads / LPT;  // tokens per pass
+  constexpr int TILE = TPP * kScoreIters;
+  const Shape& sh = p.sh;
+
+  const int tile = blockIdx.x % p.n_tiles;
+  const size_t head = blockIdx.x / p.n_tiles;  // b * Hkv + kv
+  const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
+  const int c = threadIdx.x % LPT;
+  const int tl = threadIdx.x / LPT;
+  const int t0 = tile * TILE;
+
+  float qv[G][E];
+#pragma unroll
+  for (int h = 0; h < G; h++) {
+    const float* qrow = p.qr + ((size_t)b * sh.Hq + (size_t)kv * G + h) * sh.D;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      const int j = c * E + e;
+      qv[h][e] = (j < p.d) ? qrow[j] : 0.f;
+    }
+  }
+
+  const char* panel = static_cast<const char*>(p.kcache) +
+                      head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes;
+  u32x4 x[kScoreIters];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; it++) {
+    const int t = t0 + it * TPP + tl;
+    if (t < sh.S)
+      x[it] = *reinterpret_cast<const u32x4*>(panel + ((size_t)t * LPT + c) * 16);
+    else
+      x[it] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  float* srow = p.scores + ((size_t)b * sh.Hq + (size_t)kv * G) * sh.S;
+#pragma unroll
+  for (int it = 0; it < kScoreIters; it++) {
+    float f[E];
+    unpack16<DT>(x[it], f);
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; e++) a = fmaf(qv[h][e], f[e], a);
+      s[h] = group_sum<LPT>(a);
+    }
+    const int t = t0 + it * TPP + tl;
+    if (t < sh.S) {
+#pragma unroll
+      for (int h = 0; h < G; h++)
+        if (c == (h % LPT)) srow[(size_t)h * sh.S + t] = s[h];
+    }
+  }
+}
+
+// Any d (including d > dp): one thread per token, element loads.
+template <int DT>
+__global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParams p) {
+  const Shape& sh = p.sh;
+  const int tile = blockIdx.x % p.n_tiles;
+  const size_t head = blockIdx.x / p.n_tiles;
+  const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
+  const int t = tile * kScoreThreads + threadIdx.x;
+  if (t >= sh.S) return;
+  for (int h = 0; h < sh.g; h++) {
+    const size_t qh = (size_t)b * sh.Hq + (size_t)kv * sh.g + h;
+    const float* qrow = p.qr + qh * sh.D;
+    float a = 0.f;
+    for (int j = 0; j < p.d; j++)
+      a = fmaf(qrow[j], load_elem<DT>(p.kcache, sh.kl.at(head, (size_t)t, j)), a);
+    p.scores[qh * sh.S + t] = a;
+  }
+}
+
+template <int DT, int LPT>
+hipError_t launch_lpt(ScoreParams p, hipStream_t st) {
+  constexpr int TILE = (kScoreThreads / LPT) * kScoreIters;
+  p.n_tiles = (p.sh.S + TILE - 1) / TILE;
+  const dim3 grid((unsigned)((size_t)p.n_tiles * p.sh.B * p.sh.Hkv));
+  switch (p.sh.g) {
+    case 1: score_panel_kernel<DT, LPT, 1><<<grid, kScoreThreads, 0, st>>>(p); break;
+    case 2: score_panel_kernel<DT, LPT, 2><<<grid, kScoreThreads, 0, st>>>(p); break;
+    case 4: score_panel_kernel<DT, LPT, 4><<<grid, kScoreThreads, 0, st>>>(p); break;
+    default: score_panel_kernel<DT, LPT, 8><<<grid, kScoreThreads, 0, st>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(ScoreParams p, hipStream_t st) {
+  const int lpt = p.sh.dp * Elem<DT>::kBytes / 16;
+  const int g = p.sh.g;
+  const bool fast = p.d <= p.sh.dp && (g == 1 || g == 2 || g == 4 || g == 8) &&
+                    (lpt == 2 || lpt == 4 || lpt == 8 || lpt == 16);
+  if (fast) {
+    switch (lpt) {
+      case 2: return launch_lpt<DT, 2>(p, st);
+      case 4: return launch_lpt<DT, 4>(p, st);
+      case 8: return launch_lpt<DT, 8>(p, st);
+      default: return launch_lpt<DT, 16>(p, st);
+    }
+  }
+  p.n_tiles = (p.sh.S + kScoreThreads - 1) / kScoreThreads;
+  const dim3 grid((unsigned)((size_t)p.n_tiles * p.sh.B * p.sh.Hkv));
+  score_generic_kernel<DT><<<grid, kScoreThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreParams& p, hipStream_t st) {
+  switch (p.sh.dtype) {
+    case F32: return launch_dt<F32>(p, st);
+    case F16: return launch_dt<F16>(p, st);
+    default: return launch_dt<BF16>(p, st);
+  }
+}
+
+}  // namespace loki

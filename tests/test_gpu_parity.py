@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Per-kernel tests isolate each step (layout, query rotation, append, scores,
+top-k on fixed scores, attention on fixed index sets); end-to-end tests run
+loki_decode / loki_decode_append on seeded inputs spanning several tiles with
+ragged tails, the degenerate cases, and the five full-size workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import loki_oracle as oracle
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_decode_attention_rotate_amd as loki
+    return loki
+
+
+def _small(dtype="f16", **kw):
+    base = dict(B=2, Hq=4, Hkv=2, D=128, S=3000, d=32, k=300, dtype=dtype, tau=40.0,
+                n_calib=2048)
+    base.update(kw)
+    return W.custom(name="small", wid=200, **base)
+
+
+# ------------------------------------------------------------------ layout
+
+@pytest.mark.parametrize("dtype,dp,D", [("f16", 32, 128), ("bf16", 16, 128), ("f32", 32, 128),
+                                        ("f16", 128, 128), ("f32", 8, 64), ("bf16", 64, 64)])
+def test_pack_unpack_layout(L, dtype, dp, D):
+    wl = _small(dtype, D=D, S=77, S_cap=100)
+    H.log(f"pack/unpack {dtype} dp={dp} D={D}")
+    x = W.generate(wl)
+    desc = H.make_desc(wl, dp)
+    rows = H.to_device(x["krot"][:, :, :77], dtype)
+    cache = L.empty_kcache(desc)
+    L.pack_kcache(rows, cache, desc)
+    back = L.unpack_kcache(cache, 77, desc)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.to_host(back, dtype), x["krot"][:, :, :77])
+    # documented layout: per (b, kv) [S_cap, dp] panel then [S_cap, D - dp]
+    flat = H.to_host(cache, dtype).reshape(wl.B * wl.Hkv, 100 * D)
+    src = x["krot"][:, :, :77].reshape(wl.B * wl.Hkv, 77, D)
+    for hd in range(wl.B * wl.Hkv):
+        panel = flat[hd, :100 * dp].reshape(100, dp)
+        rest = flat[hd, 100 * dp:].reshape(100, D - dp)
+        assert np.array_equal(panel[:77], src[hd, :, :dp])
+        assert np.array_equal(rest[:77], src[hd, :, dp:])
+
+
+# --------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 4), ("f16", 8, 2), ("bf16", 6, 3)])
+def test_rotate_query(L, dtype, Hq, Hkv):
+    wl = _small(dtype, Hq=Hq, Hkv=Hkv, B=5, S=64, k=8)
+    H.log(f"rotate {dtype} Hq={Hq} Hkv={Hkv}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    qr = L.rotate_query(dev["q"], dev["P"], dev["desc"]).cpu().numpy().astype(np.float64)
+    ref = oracle.rotate_queries(x["q"], x["P"], Hkv, dtype)
+    q64 = W.from_storage(x["q"], dtype)
+    P = x["P"].astype(np.float64)
+    g = Hq // Hkv
+    bound = np.stack([np.abs(q64[:, h]) @ np.abs(P[h // g]) for h in range(Hq)], axis=1)
+    assert np.all(np.abs(qr - ref) <= 2 * 128 * 2.0 ** -24 * bound + 1e-30)
+
+
+# ----------------------------------------------------------------- append
+
+@pytest.mark.parametrize("dtype,dp", [("f32", 32), ("f16", 32), ("bf16", 32), ("f16", 128),
+                                      ("bf16", 16)])
+def test_append_row(L, dtype, dp):
+    wl = _small(dtype, S=50, S_cap=64, k=5, append=True, B=3, Hq=4, Hkv=4)
+    H.log(f"append {dtype} dp={dp}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x, dp)
+    desc = dev["desc"]
+    pos = 49
+    L.append(dev["k_new"], dev["v_new"], dev["P"], dev["kcache"], dev["v"], pos, desc)
+    rows = L.unpack_kcache(dev["kcache"], 64, desc.with_seq_len(64))
+    torch.cuda.synchronize()
+    got = H.to_host(rows, dtype)
+    kr, vr = oracle.append_rows(x["k_new"], x["v_new"], x["P"], dtype)
+    g = W.from_storage(got[:, :, pos], dtype)
+    r = W.from_storage(kr, dtype)
+    # at most one unit in the last place of the storage dtype (fp32 product vs exact)
+    mant = {"f32": 23, "f16": 10, "bf16": 7}[dtype]
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - mant)
+    assert np.all(np.abs(g - r) <= ulp)
+    frac_exact = np.mean(g == r)
+    H.log(f"  appended elements equal to the oracle's rounding: {frac_exact:.5f}")
+    assert frac_exact > 0.99
+    assert np.array_equal(H.to_host(dev["v"], dtype)[:, :, pos], vr)
+    # other rows untouched
+    keep = np.ones(64, bool)
+    keep[pos] = False
+    assert np.array_equal(got[:, :, keep], x["krot"][:, :, keep])
+
+
+# ------------------------------------------------------------------ scores
+
+@pytest.mark.parametrize("dtype,g,d,dp", [("f16", 1, 32, 32), ("bf16", 4, 32, 32),
+                                          ("f32", 2, 32, 32), ("f16", 8, 20, 32),
+                                          ("f16", 1, 48, 32), ("bf16", 1, 16, 16),
+                                          ("f32", 1, 128, 128), ("f16", 3, 32, 32)])
+def test_scores(L, dtype, g, d, dp):
+    wl = _small(dtype, Hq=2 * g, Hkv=2, S=2500, k=50)
+    H.log(f"scores {dtype} g={g} d={d} dp={dp}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x, dp)
+    desc = dev["desc"]
+    qr_dev = L.rotate_query(dev["q"], dev["P"], desc)
+    s = L.score(qr_dev, dev["kcache"], d, desc).cpu().numpy().astype(np.float64)
+    r = oracle.decode(x["q"], x["krot"], x["v"], x["P"], d, 50, dtype)
+    k64 = W.from_storage(x["krot"], dtype)
+    qr = r["qr"]
+    # fp32 bound: error of the fp32 query rotation plus the fp32 dot product
+    mag = np.stack([np.einsum("bj,btj->bt", np.abs(qr[:, h, :d]), np.abs(k64[:, h // g, :, :d]))
+                    for h in range(wl.Hq)], axis=1)
+    assert np.all(np.abs(s - r["scores"]) <= 4 * (128 + d) * 2.0 ** -24 * mag + 1e-30)
+
+
+# ------------------------------------------------------------------- top-k
+
+def _topk_cases():
+    g = np.random.default_rng(123)
+    cases = []
+    for S, k in [(1, 1), (7, 3), (64, 64), (1000, 125), (4096, 512), (5000, 1), (8192, 1024),
+                 (8193, 4000), (20000, 2500), (32768, 4096), (40000, 5000)]:
+        cases.append((f"normal-{S}-{k}", g.standard_normal((3, S)).astype(np.float32), k))
+    cases.append(("ties", g.integers(-3, 4, (4, 3000)).astype(np.float32), 700))
+    cases.append(("all-equal", np.full((2, 2048), 0.5, np.float32), 100))
+    z = g.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), (2, 1500))
+    cases.append(("signed-zero", z, 900))
+    hh = g.standard_normal((2, 32768)).astype(np.float32)
+    hh[:, g.choice(32768, 655, replace=False)] *= 16.0
+    cases.append(("heavy", hh, 4096))
+    cases.append(("tiny-range", (1.0 + g.integers(0, 4, (2, 5000)) * 2.0 ** -23).astype(np.float32), 1234))
+    return cases
+
+
+@pytest.mark.parametrize("name,s,k", _topk_cases(), ids=[c[0] for c in _topk_cases()])
+def test_topk_bit_exact(L, name, s, k):
+    H.log(f"topk {name} S={s.shape[1]} k={k}")
+    rows, S = s.shape
+    desc = L.Desc(batch=1, n_q_heads=rows, n_kv_heads=1, head_dim=128, seq_len=S,
+                  seq_capacity=S, panel_dim=32, dtype=L.F16)
+    sd = torch.from_numpy(s).cuda().reshape(1, rows, S)
+    idx = L.topk(sd, k, desc).cpu().numpy()[0]
+    ref = oracle.topk_rows(s.astype(np.float64), k)
+    assert np.array_equal(idx, ref)
+
+
+# --------------------------------------------------------- attention alone
+
+@pytest.mark.parametrize("dtype,D,k,g", [("f16", 128, 300, 1), ("bf16", 128, 128, 2),
+                                         ("f32", 128, 1, 1), ("f32", 64, 257, 1),
+                                         ("f16", 64, 640, 4), ("bf16", 128, 1000, 1)])
+def test_attend_given_index_sets(L, dtype, D, k, g):
+    wl = _small(dtype, D=D, Hq=2 * g, Hkv=2, S=1500, k=k)
+    H.log(f"attend {dtype} D={D} k={k} g={g}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    rg = np.random.default_rng(7)
+    idx = np.stack([np.stack([rg.choice(1500, k, replace=False) for _ in range(wl.Hq)])
+                    for _ in range(wl.B)]).astype(np.int32)
+    qr = L.rotate_query(dev["q"], dev["P"], dev["desc"])
+    out = L.attend(qr, dev["kcache"], dev["v"], torch.from_numpy(idx).cuda(), dev["desc"])
+    out = out.cpu().numpy().astype(np.float64)
+    ref = oracle.attend_given(x["q"], x["krot"], x["v"], x["P"], idx, dtype)
+    err = H.rel_err_rows(out, ref)
+    H.log(f"  max rel err {err.max():.2e}")
+    assert err.max() < H.OUT_TOL[dtype]
+
+
+def test_attend_skips_out_of_range_indices(L):
+    wl = _small("f16", S=600, k=64)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    rg = np.random.default_rng(8)
+    idx = np.stack([np.stack([rg.choice(600, 64, replace=False) for _ in range(4)])
+                    for _ in range(2)]).astype(np.int32)
+    bad = idx.copy()
+    bad[:, :, 5] = -3
+    bad[:, :, 9] = 600
+    qr = L.rotate_query(dev["q"], dev["P"], dev["desc"])
+    out = L.attend(qr, dev["kcache"], dev["v"], torch.from_numpy(bad).cuda(), dev["desc"])
+    out = out.cpu().numpy().astype(np.float64)
+    keep = np.delete(idx, [5, 9], axis=2)
+    ref = oracle.attend_given(x["q"], x["krot"], x["v"], x["P"], keep, "f16")
+    assert H.rel_err_rows(out, ref).max() < 2e-3
+
+
+# --------------------------------------------------------------- end to end
+
+E2E = {
+    "f16-ragged": dict(dtype="f16"),
+    "bf16-ragged": dict(dtype="bf16"),
+    "f32-ragged": dict(dtype="f32", tau=20.0),
+    "gqa4-bf16": dict(dtype="bf16", Hq=8, Hkv=2, S=5000, k=700),
+    "gqa8-f16": dict(dtype="f16", Hq=16, Hkv=2, S=2100, k=130),
+    "gqa3-generic": dict(dtype="f16", Hq=6, Hkv=2, S=1100, k=100),
+    "d-below-panel": dict(dtype="f16", d=20),
+    "d-above-panel": dict(dtype="f16", d=48),
+    "d-full": dict(dtype="f16", d=128),
+    "k-full": dict(dtype="f16", S=700, k=700),
+    "k-one": dict(dtype="bf16", k=1),
+    "seq-one": dict(dtype="f16", S=1, k=1, d=8),
+    "cap-above-seq": dict(dtype="f16", S=1900, S_cap=2600, k=200),
+    "d64-head": dict(dtype="f16", D=64, d=16, tau=20.0),
+    "long-11k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=11000, k=1375),
+    "long-40k": dict(dtype="f16", B=1, Hq=1, Hkv=1, S=40000, k=5000),
+}
+
+
+@pytest.mark.parametrize("case", list(E2E), ids=list(E2E))
+def test_decode_end_to_end(L, case):
+    wl = _small(**E2E[case])
+    H.log(f"decode {case}: {W.describe(wl)}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {res}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_decode_append_end_to_end(L, dtype):
+    wl = _small(dtype, S=2600, S_cap=3000, k=333, append=True, heavy_frac=0.02)
+    H.log(f"decode_append {dtype}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {res}")
+
+
+def test_softmax_scale_argument(L):
+    wl = _small("f16", S=900, k=90)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    dev["desc"] = H.make_desc(wl, 32, scale=0.3)
+    out, idx = H.run_decode(wl, dev)
+    ref = oracle.attend_given(x["q"], x["krot"], x["v"], x["P"], idx, "f16", scale=0.3)
+    assert H.rel_err_rows(out, ref).max() < 2e-3
+
+
+def test_zero_query_ties_to_first_tokens(L):
+    wl = _small("f16", S=1000, k=100)
+    x = W.generate(wl)
+    x["q"][:] = 0
+    dev = H.upload(wl, x)
+    out, idx = H.run_decode(wl, dev)
+    assert np.array_equal(idx, np.broadcast_to(np.arange(100, dtype=np.int32), idx.shape))
+    ref = W.from_storage(x["v"], "f16")[:, :, :100].mean(axis=2)
+    ref = np.repeat(ref, 2, axis=1)
+    assert H.rel_err_rows(out, ref).max() < 1e-5
+
+
+def test_repeat_runs_are_bit_identical(L):
+    wl = _small("bf16", S=4096, k=512, B=4, Hq=8, Hkv=8)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    o1, i1 = H.run_decode(wl, dev)
+    for _ in range(5):
+        o2, i2 = H.run_decode(wl, dev)
+        assert np.array_equal(o1, o2) and np.array_equal(i1, i2)
+
+
+# ---------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(L, name):
+    wl = W.get(name)
+    H.log(f"workload {name}: generating")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    H.log(f"workload {name}: decode on GPU")
+    out, idx = H.run_decode(wl, dev)
+    del dev
+    torch.cuda.empty_cache()
+    H.log(f"workload {name}: oracle")
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {name}: {res}")

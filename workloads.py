@@ -22,8 +22,10 @@ Storage arrays: f32 -> float32, f16 -> float16, bf16 -> uint16 (raw bits).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -94,6 +96,10 @@ def custom(name="custom", wid=100, **kw) -> Workload:
                 n_calib=1024)
     base.update(kw)
     return Workload(name, wid, **base)
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def rng(entropy: int, *key: int) -> np.random.Generator:
@@ -190,28 +196,33 @@ def generate(wl: Workload, entropy: int = 0, with_raw_keys: bool = False) -> Dic
         out["k_new"] = np.zeros((B, Hkv, D), st)
         out["v_new"] = np.zeros((B, Hkv, D), st)
 
-    for kv in range(Hkv):
+    def one_head(kv: int, b: int) -> None:
         U, P32 = cal[kv]
-        P64 = P32.astype(np.float64)
-        for b in range(B):
-            K = draw_keys(rng(entropy, wl.wid, ROLE_K, kv, b), n_prefill, U, sig)
-            if wl.heavy_frac > 0:
-                n_heavy = int(round(wl.heavy_frac * n_prefill))
-                pos = rng(entropy, wl.wid, ROLE_HEAVY, kv, b).choice(n_prefill, n_heavy,
-                                                                      replace=False)
-                K[pos] *= wl.heavy_scale
-            krot[b, kv, :n_prefill] = to_storage(K @ P64, wl.dtype)
-            v[b, kv, :n_prefill] = to_storage(
-                rng(entropy, wl.wid, ROLE_V, kv, b).standard_normal((n_prefill, D)), wl.dtype)
+        K = draw_keys(rng(entropy, wl.wid, ROLE_K, kv, b), n_prefill, U, sig)
+        if wl.heavy_frac > 0:
+            n_heavy = int(round(wl.heavy_frac * n_prefill))
+            pos = rng(entropy, wl.wid, ROLE_HEAVY, kv, b).choice(n_prefill, n_heavy, replace=False)
+            K[pos] *= wl.heavy_scale
+        krot[b, kv, :n_prefill] = to_storage(K @ P32.astype(np.float64), wl.dtype)
+        v[b, kv, :n_prefill] = to_storage(
+            rng(entropy, wl.wid, ROLE_V, kv, b).standard_normal((n_prefill, D)), wl.dtype)
+        if k64 is not None:
+            k64[b, kv, :n_prefill] = K
+        if wl.append:
+            gnew = rng(entropy, wl.wid, ROLE_NEW, kv, b)
+            kn = draw_keys(gnew, 1, U, sig)[0]
+            out["k_new"][b, kv] = to_storage(kn, wl.dtype)
+            out["v_new"][b, kv] = to_storage(gnew.standard_normal(D), wl.dtype)
             if k64 is not None:
-                k64[b, kv, :n_prefill] = K
-            if wl.append:
-                gnew = rng(entropy, wl.wid, ROLE_NEW, kv, b)
-                kn = draw_keys(gnew, 1, U, sig)[0]
-                out["k_new"][b, kv] = to_storage(kn, wl.dtype)
-                out["v_new"][b, kv] = to_storage(gnew.standard_normal(D), wl.dtype)
-                if k64 is not None:
-                    k64[b, kv, S - 1] = from_storage(out["k_new"][b, kv], wl.dtype)
+                k64[b, kv, S - 1] = from_storage(out["k_new"][b, kv], wl.dtype)
+
+    # every (b, kv) draws from its own seeded stream, so the thread order does
+    # not change the result
+    jobs = [(kv, b) for kv in range(Hkv) for b in range(B)]
+    with cf.ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(lambda a: one_head(*a), jobs))
+    for kv in range(Hkv):
+        U = cal[kv][0]
         for j in range(wl.g):
             h = kv * wl.g + j
             for b in range(B):
