@@ -105,7 +105,7 @@ def main():
     v0 = up(x["v"])
     sets = [(kc0, v0)] + [(kc0.clone(), v0.clone()) for _ in range(args.sets - 1)]
     q = up(x["q"])
-    P = torch.from_numpy(x["P"]).to(dev)
+    P = torch.from_numpy(np.ascontiguousarray(x["P"])).to(dev)
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
     idx = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device=dev)
     ws = loki.empty_workspace(desc, wl.d, wl.k)
@@ -156,6 +156,10 @@ def main():
     n_ph = len(PHASES)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph + 1)]
            for _ in range(args.steps)]
+    for row in evs:          # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
     phase_ms = np.zeros(n_ph)
     for i in range(args.steps):
         loki.profile_events(evs[i])

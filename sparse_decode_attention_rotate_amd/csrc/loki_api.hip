@@ -69,6 +69,10 @@ int check_desc(const loki_desc* d, Shape* sh) {
     return fail(LOKI_EINVAL, "need 1 <= seq_len (%d) <= seq_capacity (%d) <= 2^30",
                 d->seq_len, d->seq_capacity);
   const int dp = d->panel_dim, eb = elem_bytes(d->dtype);
+  // one (b, kv) block of either cache is addressed with 32-bit byte offsets
+  if ((size_t)d->seq_capacity * d->head_dim * eb >= ((size_t)1 << 31))
+    return fail(LOKI_EUNSUPPORTED, "seq_capacity %d: one head's cache exceeds 2 GiB",
+                d->seq_capacity);
   if (dp < 1 || dp > d->head_dim || (dp & (dp - 1)) != 0 || dp * eb < 16)
     return fail(LOKI_EINVAL,
                 "panel_dim %d must be a power of two <= head_dim with panel_dim*elem >= 16", dp);

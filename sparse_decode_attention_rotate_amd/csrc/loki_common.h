@@ -94,6 +94,26 @@ template <int DT> __device__ __forceinline__ void copy_elem(void* dst, size_t di
     static_cast<unsigned short*>(dst)[di] = static_cast<const unsigned short*>(src)[si];
 }
 
+// ---------------------------------------------------------------- buffer loads
+//
+// Raw buffer loads carry a hardware range check: a load whose byte offset lies
+// past the descriptor's size returns zeros and touches no memory.  Loads of
+// rows that do not exist (tails, invalid indices) therefore need no branch,
+// which keeps every load of a batch in flight together.
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 of a gfx9 buffer descriptor: 32-bit data format, no swizzle
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
 // ---------------------------------------------------------------- cross-lane
 
 // DPP move within a row of 16 lanes (ctrl is the gfx9 DPP control word).

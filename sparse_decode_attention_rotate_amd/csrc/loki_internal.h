@@ -24,6 +24,7 @@ struct ProjectParams {
   void* vcache;
   int pos;            // append row
   int bb;             // batch rows per workgroup
+  hipStream_t stream;
   Shape sh;
 };
 
@@ -71,6 +72,6 @@ hipError_t launch_attend(const AttendParams& p, hipStream_t st);
 hipError_t launch_layout(const LayoutParams& p, hipStream_t st);
 
 // Rows of the selected set processed by one attention workgroup.
-constexpr int kAttendChunk = 128;
+constexpr int kAttendChunk = 512;
 
 }  // namespace loki

@@ -7,9 +7,10 @@
 // into the rotated cache (poster page, "Loki's Computational Cost": the
 // KV-cache append is part of every decode step).
 //
-// One workgroup per (KV head, block of batch rows): the g query rows of each
-// batch entry (and the new key, when appending) are staged in LDS as fp32 and
-// multiplied by P[kv], read once per workgroup with coalesced 512-byte rows.
+// One workgroup per (KV head, block of batch rows): P[kv] (fp32) is staged in
+// LDS with 16-byte loads all in flight at once, the g query rows of each batch
+// entry (and the new key, when appending) are staged as fp32, and each thread
+// forms one output coordinate for its rows.
 #include "loki_internal.h"
 
 namespace loki {
@@ -19,11 +20,13 @@ namespace {
 constexpr int kProjThreads = 256;
 constexpr int kMaxRows = 32;
 
-template <int DT, int D>
+template <int DT, int D, int ACC>
 __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectParams p) {
-  constexpr int RG = kProjThreads / D;  // row groups
-  constexpr int ACC = kMaxRows / RG;
+  constexpr int RG = kProjThreads / D;             // row groups
+  constexpr int PV = D * D / 4 / kProjThreads;     // 16-byte pieces of P per thread
+  static_assert(ACC * RG <= kMaxRows, "row buffer too small");
   __shared__ float xs[kMaxRows][D];
+  __shared__ float ps[D * D];
 
   const Shape& sh = p.sh;
   const int kv = blockIdx.x;
@@ -33,29 +36,46 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectParams p) 
   const int per_b = nq + (p.k_new ? 1 : 0);
   const int R = nb * per_b;
 
-  for (int e = threadIdx.x; e < R * D; e += kProjThreads) {
+  // P[kv] -> LDS: every 16-byte load issued before the first is consumed
+  const u32x4* Pk = reinterpret_cast<const u32x4*>(p.P + (size_t)kv * D * D);
+  u32x4 pv[PV];
+#pragma unroll
+  for (int u = 0; u < PV; u++) pv[u] = Pk[u * kProjThreads + threadIdx.x];
+
+  // rows (queries, then the new key) as fp32; rows >= R are zero
+  for (int e = threadIdx.x; e < ACC * RG * D; e += kProjThreads) {
     const int r = e / D, i = e % D;
-    const int b = b0 + r / per_b, which = r % per_b;
-    float x;
-    if (which < nq)
-      x = load_elem<DT>(p.q, ((size_t)b * sh.Hq + (size_t)kv * sh.g + which) * D + i);
-    else
-      x = load_elem<DT>(p.k_new, ((size_t)b * sh.Hkv + kv) * D + i);
+    float x = 0.f;
+    if (r < R) {
+      const int b = b0 + r / per_b, which = r % per_b;
+      if (which < nq)
+        x = load_elem<DT>(p.q, ((size_t)b * sh.Hq + (size_t)kv * sh.g + which) * D + i);
+      else
+        x = load_elem<DT>(p.k_new, ((size_t)b * sh.Hkv + kv) * D + i);
+    }
     xs[r][i] = x;
   }
+#pragma unroll
+  for (int u = 0; u < PV; u++)
+    reinterpret_cast<u32x4*>(ps)[u * kProjThreads + threadIdx.x] = pv[u];
   __syncthreads();
 
+  // thread (j, rg) forms coordinate j of rows rg, rg + RG, ...: branch-free
   const int j = threadIdx.x % D, rg = threadIdx.x / D;
   float acc[ACC];
 #pragma unroll
   for (int a = 0; a < ACC; a++) acc[a] = 0.f;
-  const float* Pk = p.P + (size_t)kv * D * D;
-  for (int i = 0; i < D; i++) {
-    const float pij = Pk[(size_t)i * D + j];
+#pragma unroll 2
+  for (int i = 0; i < D; i += 4) {
+    const float p0 = ps[(i + 0) * D + j], p1 = ps[(i + 1) * D + j];
+    const float p2 = ps[(i + 2) * D + j], p3 = ps[(i + 3) * D + j];
 #pragma unroll
     for (int a = 0; a < ACC; a++) {
-      const int r = rg + a * RG;
-      if (r < R) acc[a] = fmaf(xs[r][i], pij, acc[a]);
+      const float4 x4 = *reinterpret_cast<const float4*>(&xs[rg + a * RG][i]);
+      acc[a] = fmaf(x4.x, p0, acc[a]);
+      acc[a] = fmaf(x4.y, p1, acc[a]);
+      acc[a] = fmaf(x4.z, p2, acc[a]);
+      acc[a] = fmaf(x4.w, p3, acc[a]);
     }
   }
 
@@ -82,13 +102,27 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectParams p) 
   }
 }
 
-template <int DT>
-hipError_t launch_dt(const ProjectParams& p, dim3 grid, hipStream_t st) {
-  if (p.sh.D == 128)
-    project_kernel<DT, 128><<<grid, kProjThreads, 0, st>>>(p);
+template <int DT, int D>
+hipError_t launch_d(const ProjectParams& p, dim3 grid, int rows) {
+  constexpr int RG = kProjThreads / D;
+  const int acc = (rows + RG - 1) / RG;
+  hipStream_t st = p.stream;
+  if (acc <= 1)
+    project_kernel<DT, D, 1><<<grid, kProjThreads, 0, st>>>(p);
+  else if (acc <= 2)
+    project_kernel<DT, D, 2><<<grid, kProjThreads, 0, st>>>(p);
+  else if (acc <= 4)
+    project_kernel<DT, D, 4><<<grid, kProjThreads, 0, st>>>(p);
+  else if (acc <= 8)
+    project_kernel<DT, D, 8><<<grid, kProjThreads, 0, st>>>(p);
   else
-    project_kernel<DT, 64><<<grid, kProjThreads, 0, st>>>(p);
+    project_kernel<DT, D, kMaxRows / RG><<<grid, kProjThreads, 0, st>>>(p);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const ProjectParams& p, dim3 grid, int rows) {
+  return p.sh.D == 128 ? launch_d<DT, 128>(p, grid, rows) : launch_d<DT, 64>(p, grid, rows);
 }
 
 }  // namespace
@@ -104,10 +138,12 @@ hipError_t launch_project(const ProjectParams& p0, hipStream_t st) {
   if (p.bb > p.sh.B) p.bb = p.sh.B;
   if (p.bb < 1) return hipErrorInvalidValue;  // g too large for one workgroup
   dim3 grid(p.sh.Hkv, (p.sh.B + p.bb - 1) / p.bb);
+  p.stream = st;
+  const int rows = p.bb * per_b;
   switch (p.sh.dtype) {
-    case F32: return launch_dt<F32>(p, grid, st);
-    case F16: return launch_dt<F16>(p, grid, st);
-    default: return launch_dt<BF16>(p, grid, st);
+    case F32: return launch_dt<F32>(p, grid, rows);
+    case F16: return launch_dt<F16>(p, grid, rows);
+    default: return launch_dt<BF16>(p, grid, rows);
   }
 }
 

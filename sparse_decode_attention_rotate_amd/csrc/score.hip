@@ -39,21 +39,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     const float* qrow = p.qr + ((size_t)b * sh.Hq + (size_t)kv * G + h) * sh.D;
 #pragma unroll
     for (int e = 0; e < E; e++) {
-      const int j = c * E + e;
-      qv[h][e] = (j < p.d) ? qrow[j] : 0.f;
+      const int j = c * E + e;  // < dp <= D: always inside the row
+      const float v = qrow[j];
+      qv[h][e] = (j < p.d) ? v : 0.f;
     }
   }
 
-  const char* panel = static_cast<const char*>(p.kcache) +
-                      head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes;
+  // the panel of this (b, kv): S_cap rows of LPT*16 bytes; tokens >= S read as zeros
+  const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
+                                 head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
+                             (uint32_t)((size_t)sh.S_cap * LPT * 16));
   u32x4 x[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; it++) {
     const int t = t0 + it * TPP + tl;
-    if (t < sh.S)
-      x[it] = *reinterpret_cast<const u32x4*>(panel + ((size_t)t * LPT + c) * 16);
-    else
-      x[it] = u32x4{0u, 0u, 0u, 0u};
+    x[it] = load16(prs, t < sh.S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
   }
 
   float* srow = p.scores + ((size_t)b * sh.Hq + (size_t)kv * G) * sh.S;

@@ -27,6 +27,11 @@ __device__ __forceinline__ unsigned order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// inverse of order_key (a -0 score comes back as +0)
+__device__ __forceinline__ float key_value(unsigned key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
 template <int NT, int KREG>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   constexpr int NW = NT / 64;
@@ -38,13 +43,19 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   const int S = p.S;
   const float* srow = p.scores + (size_t)blockIdx.x * S;
 
+  // all score loads of this thread in flight at once (out-of-range ones read 0)
+  const Rsrc srs = make_rsrc(srow, (uint32_t)S * 4u);
   unsigned keys[KREG > 0 ? KREG : 1];
   if constexpr (KREG > 0) {
+    float sv[KREG];
 #pragma unroll
     for (int j = 0; j < KREG; j++) {
       const int i = tid + j * NT;
-      keys[j] = (i < S) ? order_key(srow[i]) : 0u;
+      sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          srs, i < S ? (int)(i * 4) : (int)kOutOfRange, 0, 0));
     }
+#pragma unroll
+    for (int j = 0; j < KREG; j++) keys[j] = order_key(sv[j]);
   }
   auto key_of = [&](int j, int i) -> unsigned {
     if constexpr (KREG > 0)
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     const int pos = out_seen + sel_before + lane_rank(bs);
     if (sel && pos < p.k) {  // exactly k are selected; the bound only guards the row
       irow[pos] = i;
-      if (vrow) vrow[pos] = srow[i];
+      if (vrow) vrow[pos] = key_value(key);
     }
     eq_seen += tot_eq;
     out_seen += tot_sel;

@@ -54,7 +54,7 @@ def upload(wl: W.Workload, x: dict, dp: int = 32):
     """Device copies: q, packed K cache, V cache, P (and k_new / v_new)."""
     loki = _loki()
     desc = make_desc(wl, dp)
-    dev = {"desc": desc, "q": to_device(x["q"], wl.dtype), "P": torch.from_numpy(x["P"]).cuda(),
+    dev = {"desc": desc, "q": to_device(x["q"], wl.dtype), "P": torch.from_numpy(np.ascontiguousarray(x["P"])).cuda(),
            "v": to_device(x["v"], wl.dtype)}
     krot_rows = to_device(x["krot"], wl.dtype)
     dev["kcache"] = loki.empty_kcache(desc)

@@ -165,7 +165,7 @@ def calibration(wl: Workload, entropy: int = 0):
         U = basis(wl, kv, entropy)
         cal = draw_keys(rng(entropy, wl.wid, ROLE_CALIB, kv), wl.n_calib, U, sig)
         P, _ = pca_basis(cal)
-        out.append((U, P.astype(np.float32)))
+        out.append((U, np.ascontiguousarray(P, dtype=np.float32)))
     return out
 
 
@@ -189,7 +189,7 @@ def generate(wl: Workload, entropy: int = 0, with_raw_keys: bool = False) -> Dic
     krot = np.zeros((B, Hkv, cap, D), st)
     v = np.zeros((B, Hkv, cap, D), st)
     q = np.zeros((B, Hq, D), st)
-    P = np.stack([p for _, p in cal])
+    P = np.ascontiguousarray(np.stack([p for _, p in cal]))
     k64 = np.zeros((B, Hkv, S, D), np.float64) if with_raw_keys else None
     out: Dict[str, np.ndarray] = {}
     if wl.append:
