@@ -28,9 +28,10 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "Loki decode-attn µs/step & achieved HBM GB/s (% peak), Llama2-13B shape"
-PHASES = ["rotate_query", "score", "topk", "attend"]
 KERNEL_SOURCES = {"score": "score.hip", "attend": "attend.hip", "topk": "topk.hip",
-                  "rotate_query": "project.hip"}
+                  "rotate_query": "project.hip", "fused": "fused.hip"}
+KERNEL_NAMES = {"score": "score_panel_kernel", "attend": "attend_kernel", "topk": "topk_kernel",
+                "rotate_query": "project_kernel", "fused": "fused_kernel"}
 
 
 def parse():
@@ -49,7 +50,7 @@ def parse():
 def src_sha(name):
     p = os.path.join(ROOT, "sparse_decode_attention_rotate_amd", "csrc", name)
     h = hashlib.sha256(open(p, "rb").read())
-    for hdr in ["loki_common.h", "loki_internal.h"]:
+    for hdr in ["loki_common.h", "loki_internal.h", "select_core.h", "attend_core.h"]:
         h.update(open(os.path.join(ROOT, "sparse_decode_attention_rotate_amd", "csrc", hdr),
                       "rb").read())
     return h.hexdigest()[:16]
@@ -112,27 +113,33 @@ def main():
     k_new = up(x["k_new"]) if wl.append else None
     v_new = up(x["v_new"]) if wl.append else None
     stream = torch.cuda.current_stream()
-    cdesc = desc.c()
+    one_launch = loki.decode_plan(desc, wl.d, wl.k, wl.append)
     vp = ctypes.c_void_p
 
-    # pre-marshalled C-ABI arguments, one tuple per cache copy
-    calls = []
-    for kc, vc in sets:
-        if wl.append:
-            calls.append((loki.lib.loki_decode_append,
-                          (vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
-                           vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d, wl.k,
-                           vp(out.data_ptr()), vp(idx.data_ptr()), ctypes.byref(cdesc),
-                           vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))))
-        else:
-            calls.append((loki.lib.loki_decode,
-                          (vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
-                           vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()), vp(idx.data_ptr()),
-                           ctypes.byref(cdesc), vp(ws.data_ptr()), ws.numel(),
-                           vp(stream.cuda_stream))))
+    def make_calls(d_):
+        cd = d_.c()
+        calls = []
+        for kc, vc in sets:
+            if wl.append:
+                calls.append((loki.lib.loki_decode_append,
+                              (vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
+                               vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d,
+                               wl.k, vp(out.data_ptr()), vp(idx.data_ptr()), ctypes.byref(cd),
+                               vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))))
+            else:
+                calls.append((loki.lib.loki_decode,
+                              (vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                               vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()),
+                               vp(idx.data_ptr()), ctypes.byref(cd), vp(ws.data_ptr()),
+                               ws.numel(), vp(stream.cuda_stream))))
+        return cd, calls
 
-    def step(i):
-        fn, a = calls[i % len(calls)]
+    # pre-marshalled C-ABI arguments, one tuple per cache copy
+    cdesc, calls = make_calls(desc)
+    cdesc_sep, calls_sep = make_calls(desc.with_flags(loki.FLAG_SEPARATE_KERNELS))
+
+    def step(i, which=calls):
+        fn, a = which[i % len(which)]
         rc = fn(*a)
         if rc != 0:
             raise RuntimeError(f"decode failed: {loki.strerror(rc)} {loki.last_error()}")
@@ -152,34 +159,66 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- per-phase durations, events recorded by the library on the same stream
-    n_ph = len(PHASES)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ph + 1)]
-           for _ in range(args.steps)]
-    for row in evs:          # torch creates the HIP event on first record
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    phase_ms = np.zeros(n_ph)
-    for i in range(args.steps):
-        loki.profile_events(evs[i])
-        step(i)
-    loki.profile_events(None)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        for p in range(n_ph):
-            phase_ms[p] += evs[i][p].elapsed_time(evs[i][p + 1])
-    phase_us = phase_ms / args.steps * 1e3
+    # ---- separate launches: whole step, then each kernel alone, K back-to-back
+    # launches between two events on the launch stream (as a kernel trace sees them)
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps * 1e3
+
+    sep_step_us = timed(lambda i: step(i, calls_sep))
+    lib = loki.lib
+    qr = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    scores = torch.empty((wl.B, wl.Hq, wl.S), dtype=torch.float32, device=dev)
+    sel = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.float32, device=dev)
+    cd = ctypes.byref(cdesc)
+    st = vp(stream.cuda_stream)
+    P_, q_, qr_, sc_, idx_, sel_, out_, ws_ = (vp(t.data_ptr()) for t in
+                                               (P, q, qr, scores, idx, sel, out, ws))
+    kcs = [vp(kc.data_ptr()) for kc, _ in sets]
+    vcs = [vp(vc.data_ptr()) for _, vc in sets]
+    split = True  # panel_dim = d: the step uses the split attention variant
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"{loki.strerror(rc)} {loki.last_error()}")
+
+    lib.loki_decode(q_, kcs[0], vcs[0], P_, wl.d, wl.k, out_, idx_, ctypes.byref(cdesc_sep),
+                    ws_, ws.numel(), st)
+    chk(lib.loki_rotate_query(q_, P_, qr_, cd, st))
+    chk(lib.loki_score(qr_, kcs[0], wl.d, sc_, cd, st))
+    chk(lib.loki_topk(sc_, wl.k, idx_, sel_, cd, st))
+    per_kernel = {
+        "rotate_query": timed(lambda i: lib.loki_rotate_query(q_, P_, qr_, cd, st)),
+        "score": timed(lambda i: lib.loki_score(qr_, kcs[i % len(kcs)], wl.d, sc_, cd, st)),
+        "topk": timed(lambda i: lib.loki_topk(sc_, wl.k, idx_, sel_, cd, st)),
+        "attend": timed(lambda i: lib.loki_attend(qr_, kcs[i % len(kcs)], vcs[i % len(vcs)], idx_,
+                                                  sel_ if split else None, wl.k, out_, cd, ws_,
+                                                  ws.numel(), st)),
+    }
+    per_kernel = {n: round(u, 2) for n, u in per_kernel.items()}
 
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()
     score_bytes = es * wl.B * wl.Hkv * wl.S * wl.d
     attend_bytes = es * wl.B * wl.Hq * 2 * wl.k * wl.D
-    per_kernel_bytes = {"score": score_bytes, "attend": attend_bytes}
-    dom = max(["score", "attend"], key=lambda n: phase_us[PHASES.index(n)])
-    dom_us = phase_us[PHASES.index(dom)]
-    achieved = per_kernel_bytes[dom] / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name, dom, per_kernel_bytes[dom])
+    if one_launch:
+        # the step is one kernel: K back-to-back launches timed above
+        dom, dom_us, dom_bytes = "fused", ms_per_step * 1e3, alg_bytes
+        kernels = {"fused": round(dom_us, 2)}
+    else:
+        per_kernel_bytes = {"score": score_bytes, "attend": attend_bytes}
+        dom = max(["score", "attend"], key=lambda n: per_kernel[n])
+        dom_us, dom_bytes = per_kernel[dom], per_kernel_bytes[dom]
+        kernels = per_kernel
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name, dom, dom_bytes)
 
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -199,12 +238,14 @@ def main():
         "data": "synthetic",
         "config": {**W.describe(wl), "algorithmic_bytes_per_step": alg_bytes,
                    "cache_copies_cycled": args.sets},
-        "per_kernel_us": {n: round(float(u), 2) for n, u in zip(PHASES, phase_us)},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "launch_plan": "one kernel" if one_launch else "separate kernels",
+        "kernel_us": kernels,
+        "separate_launches": {"us_per_step": round(sep_step_us, 2), "kernel_us": per_kernel},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": per_kernel_bytes[dom],
-                     "avg_launch_us": round(float(dom_us), 2)},
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(dom_us, 2)},
     }
 
     if not args.no_cpu_baseline:

@@ -81,7 +81,13 @@ typedef struct {
                            with d == dp. */
   int32_t dtype;        /* loki_dtype of q, K cache, V cache, k_new, v_new */
   float softmax_scale;  /* <= 0 selects 1/sqrt(D) */
+  uint32_t flags;       /* LOKI_FLAG_* bits, 0 by default */
 } loki_desc;
+
+/* loki_desc.flags: run a decode step as separate launches (query rotation,
+   scores, top-k, attention) even where the one-launch kernel applies.  Same
+   results up to fp32 summation order; for profiling the phases. */
+#define LOKI_FLAG_SEPARATE_KERNELS 1u
 
 /* Human-readable name of a status code; never NULL. */
 const char* loki_strerror(int status);
@@ -94,6 +100,16 @@ int loki_kcache_elems(const loki_desc* desc, size_t* n_elems);
 
 /* Bytes of workspace loki_decode / loki_decode_append need for (d, k). */
 int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes);
+
+/*
+ * Launch plan of a decode step: *one_launch = 1 when loki_decode (append = 0)
+ * or loki_decode_append (append = 1) with these arguments runs as a single
+ * kernel (rotation, scores in LDS, top-k, attention per (b, kv) workgroup:
+ * needs d == panel_dim, head_dim 128, Hq/Hkv in {1, 2, 4}, S <= 4096 and the
+ * group's scores within the LDS budget, no append), 0 when it runs as separate
+ * launches.
+ */
+int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_launch);
 
 /*
  * Cache layout conversion.  krot_rows [B, Hkv, n_tokens, D] row-major rotated
@@ -128,20 +144,27 @@ int loki_score(const float* qr, const void* kcache, int d, float* scores,
 /*
  * Top-k selection [A], [T], [TB]: idx[b,h,:] = the k tokens ranked first by
  * (score descending, token ascending), listed in ascending token order;
- * -0 ranks as +0.  1 <= k <= S.  Scores must not be NaN.
+ * -0 ranks as +0.  1 <= k <= S.  Scores must not be NaN.  sel_out
+ * (nullable, [B, Hq, k] fp32) receives the scores of the selected tokens in
+ * the same order (-0 as +0).
  */
-int loki_topk(const float* scores, int k, int32_t* idx, const loki_desc* desc, void* stream);
+int loki_topk(const float* scores, int k, int32_t* idx, float* sel_out, const loki_desc* desc,
+              void* stream);
 
 /*
  * Exact attention over given token sets [T], [F1]:
  * z_t = scale * sum_{j<D} qr[b,h,j] krot[b,kv,t,j] for t in idx[b,h,:],
  * out[b,h,:] = sum_t softmax(z)_t V[b,kv,t,:].  Entries of idx outside
  * [0, S) contribute zero weight (all of them outside -> NaN row).
+ * sel_scores (nullable, [B, Hq, k]): the partial logits sum_{j<dp} qr_j
+ * krot_{t,j} of the listed tokens over the leading panel_dim coordinates (what
+ * loki_score with d = panel_dim and loki_topk's sel_out give); when given, only
+ * the remaining D - panel_dim key coordinates are read.
  * Needs loki_workspace_bytes(desc, D, k) bytes of workspace.
  */
 int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
-                int k, float* out, const loki_desc* desc, void* workspace,
-                size_t workspace_bytes, void* stream);
+                const float* sel_scores, int k, float* out, const loki_desc* desc,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One full Loki decode step [A], [T], [F1]: rotate q, score all S tokens
@@ -162,16 +185,6 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
                        void* vcache, const float* P, int d, int k, float* out,
                        int32_t* idx_out, const loki_desc* desc, void* workspace,
                        size_t workspace_bytes, void* stream);
-
-/*
- * Diagnostic hook (no method content): while set, every loki_decode /
- * loki_decode_append call made by THIS thread records events[0..4] (each a
- * hipEvent_t created by the caller) on its stream: before the query rotation,
- * before the scoring, before the top-k, before the attention, and after the
- * attention.  n_events = 0 clears the hook; any other count but 5 is
- * LOKI_EINVAL.  The events stay owned by the caller.
- */
-int loki_profile_events(void* const* events, int n_events);
 
 #ifdef __cplusplus
 }

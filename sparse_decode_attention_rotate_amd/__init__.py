@@ -26,6 +26,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, F16, BF16 = 0, 1, 2
+FLAG_SEPARATE_KERNELS = 1
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 NAME_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
@@ -37,7 +38,7 @@ STATUS = {0: "LOKI_OK", -1: "LOKI_EINVAL", -2: "LOKI_EUNSUPPORTED", -3: "LOKI_EW
 EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_workspace_bytes",
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
-           "loki_profile_events"]
+           "loki_decode_plan"]
 
 
 class _CDesc(ctypes.Structure):
@@ -45,7 +46,7 @@ class _CDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("seq_len", ctypes.c_int32), ("seq_capacity", ctypes.c_int32),
                 ("panel_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -60,12 +61,12 @@ _SIG = {
     "loki_append": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _D, _vp], _i),
     "loki_rotate_query": ([_vp, _vp, _vp, _D, _vp], _i),
     "loki_score": ([_vp, _vp, _i, _vp, _D, _vp], _i),
-    "loki_topk": ([_vp, _i, _vp, _D, _vp], _i),
-    "loki_attend": ([_vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
+    "loki_topk": ([_vp, _i, _vp, _vp, _D, _vp], _i),
+    "loki_attend": ([_vp, _vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
     "loki_decode": ([_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _D, _vp, _sz, _vp], _i),
     "loki_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _D, _vp, _sz, _vp],
                            _i),
-    "loki_profile_events": ([ctypes.POINTER(_vp), _i], _i),
+    "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(_lib, _name)
@@ -92,10 +93,15 @@ class Desc:
     panel_dim: int
     dtype: int
     softmax_scale: float = 0.0
+    flags: int = 0
 
     def c(self) -> _CDesc:
         return _CDesc(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.seq_len,
-                      self.seq_capacity, self.panel_dim, self.dtype, self.softmax_scale)
+                      self.seq_capacity, self.panel_dim, self.dtype, self.softmax_scale,
+                      self.flags)
+
+    def with_flags(self, flags: int) -> "Desc":
+        return dataclasses.replace(self, flags=flags)
 
     def with_seq_len(self, s: int) -> "Desc":
         return dataclasses.replace(self, seq_len=s)
@@ -143,6 +149,14 @@ def workspace_bytes(desc: Desc, d: int, k: int) -> int:
     _check(_lib.loki_workspace_bytes(ctypes.byref(desc.c()), d, k, ctypes.byref(n)),
            "loki_workspace_bytes")
     return n.value
+
+
+def decode_plan(desc: Desc, d: int, k: int, append: bool = False) -> bool:
+    """True when the decode step runs as one kernel launch."""
+    one = ctypes.c_int()
+    _check(_lib.loki_decode_plan(ctypes.byref(desc.c()), d, k, int(append), ctypes.byref(one)),
+           "loki_decode_plan")
+    return bool(one.value)
 
 
 def empty_kcache(desc: Desc, device="cuda") -> torch.Tensor:
@@ -203,17 +217,21 @@ def score(qr, kcache, d: int, desc: Desc, scores=None, stream=None):
     return scores
 
 
-def topk(scores, k: int, desc: Desc, idx=None, stream=None):
+def topk(scores, k: int, desc: Desc, idx=None, sel_out=None, stream=None):
+    """Top-k indices [B, Hq, k] (ascending); sel_out, if given, gets their scores."""
     _expect(scores, (desc.batch, desc.n_q_heads, desc.seq_len), torch.float32, "scores")
     if idx is None:
         idx = torch.empty((desc.batch, desc.n_q_heads, k), dtype=torch.int32,
                           device=scores.device)
-    _check(_lib.loki_topk(_ptr(scores), k, _ptr(idx), ctypes.byref(desc.c()), _stream(stream)),
-           "loki_topk")
+    _check(_lib.loki_topk(_ptr(scores), k, _ptr(idx), _ptr(sel_out), ctypes.byref(desc.c()),
+                          _stream(stream)), "loki_topk")
     return idx
 
 
-def attend(qr, kcache, vcache, idx, desc: Desc, out=None, workspace=None, stream=None):
+def attend(qr, kcache, vcache, idx, desc: Desc, out=None, workspace=None, sel_scores=None,
+           stream=None):
+    """Exact attention over idx; with sel_scores (partial logits over the leading
+    panel_dim coordinates) only the remaining key coordinates are read."""
     k = idx.shape[-1]
     _expect(idx, (desc.batch, desc.n_q_heads, k), torch.int32, "idx")
     if out is None:
@@ -221,7 +239,8 @@ def attend(qr, kcache, vcache, idx, desc: Desc, out=None, workspace=None, stream
                           device=qr.device)
     if workspace is None:
         workspace = empty_workspace(desc, desc.head_dim, k, qr.device)
-    _check(_lib.loki_attend(_ptr(qr), _ptr(kcache), _ptr(vcache), _ptr(idx), k, _ptr(out),
+    _check(_lib.loki_attend(_ptr(qr), _ptr(kcache), _ptr(vcache), _ptr(idx), _ptr(sel_scores), k,
+                            _ptr(out),
                             ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
                             _stream(stream)), "loki_attend")
     return out
@@ -256,16 +275,6 @@ def decode_append(q, k_new, v_new, kcache, vcache, P, d: int, k: int, desc: Desc
                                    _ptr(workspace), workspace.numel(), _stream(stream)),
            "loki_decode_append")
     return out
-
-
-def profile_events(events) -> None:
-    """Record the 5 given torch.cuda.Event objects around the phases of the
-    following decode calls on this thread (None clears)."""
-    if events is None:
-        _check(_lib.loki_profile_events(None, 0), "loki_profile_events")
-        return
-    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
-    _check(_lib.loki_profile_events(arr, len(events)), "loki_profile_events")
 
 
 def strerror(code: int) -> str:

@@ -16,16 +16,6 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Diagnostic hook: events recorded before each phase of a decode step and
-// after the last one (loki_profile_events).
-thread_local hipEvent_t g_prof_events[5];
-thread_local int g_prof_n = 0;
-
-hipError_t mark(int i, hipStream_t st) {
-  if (g_prof_n == 5) return hipEventRecord(g_prof_events[i], st);
-  return hipSuccess;
-}
-
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -155,6 +145,20 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   const bool split = (d == sh.dp);
   float* sel = split ? reinterpret_cast<float*>(ws + w.sel) : nullptr;
 
+  if (!append && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
+    FusedParams fp{};
+    fp.q = q;
+    fp.kcache = kcache;
+    fp.vcache = vcache;
+    fp.P = P;
+    fp.out = out;
+    fp.idx_out = idx_out;
+    fp.k = k;
+    fp.scale_log2 = scale_log2(desc);
+    fp.sh = sh;
+    return hip_status(launch_fused(fp, st), "fused");
+  }
+
   ProjectParams pp{};
   pp.q = q;
   pp.k_new = append ? k_new : nullptr;
@@ -165,9 +169,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   pp.vcache = vcache;
   pp.pos = sh.S - 1;
   pp.sh = sh;
-  if ((rc = hip_status(mark(0, st), "event"))) return rc;
   if ((rc = hip_status(launch_project(pp, st), "project"))) return rc;
-  if ((rc = hip_status(mark(1, st), "event"))) return rc;
 
   ScoreParams sp{};
   sp.qr = qr;
@@ -176,7 +178,6 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   sp.d = d;
   sp.sh = sh;
   if ((rc = hip_status(launch_score(sp, st), "score"))) return rc;
-  if ((rc = hip_status(mark(2, st), "event"))) return rc;
 
   TopkParams tp{};
   tp.scores = scores;
@@ -185,7 +186,6 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   tp.S = sh.S;
   tp.k = k;
   if ((rc = hip_status(launch_topk(tp, sh.B * sh.Hq, st), "topk"))) return rc;
-  if ((rc = hip_status(mark(3, st), "event"))) return rc;
 
   AttendParams ap{};
   ap.qr = qr;
@@ -201,8 +201,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   ap.kc = kAttendChunk;
   ap.scale_log2 = scale_log2(desc);
   ap.sh = sh;
-  if ((rc = hip_status(launch_attend(ap, st), "attend"))) return rc;
-  return hip_status(mark(4, st), "event");
+  return hip_status(launch_attend(ap, st), "attend");
 }
 
 }  // namespace
@@ -222,20 +221,6 @@ const char* loki_strerror(int status) {
 
 const char* loki_last_error(void) { return g_last_error.c_str(); }
 
-int loki_profile_events(void* const* events, int n_events) {
-  if (n_events == 0) {
-    g_prof_n = 0;
-    return LOKI_OK;
-  }
-  if (n_events != 5 || !events) return fail(LOKI_EINVAL, "need 5 events (got %d)", n_events);
-  for (int i = 0; i < 5; i++) {
-    if (!events[i]) return fail(LOKI_EINVAL, "event %d is NULL", i);
-    g_prof_events[i] = (hipEvent_t)events[i];
-  }
-  g_prof_n = 5;
-  return LOKI_OK;
-}
-
 int loki_kcache_elems(const loki_desc* desc, size_t* n_elems) {
   Shape sh;
   int rc = check_desc(desc, &sh);
@@ -253,6 +238,18 @@ int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes) {
   if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
   *bytes = ws_layout(sh, k).total;
+  return LOKI_OK;
+}
+
+int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_launch) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  if (!one_launch) return fail(LOKI_EINVAL, "one_launch is NULL");
+  if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
+  if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
+  *one_launch = (!append && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) &&
+                 fused_supported(sh, d, k)) ? 1 : 0;
   return LOKI_OK;
 }
 
@@ -340,7 +337,8 @@ int loki_score(const float* qr, const void* kcache, int d, float* scores, const 
   return hip_status(launch_score(sp, (hipStream_t)stream), "score");
 }
 
-int loki_topk(const float* scores, int k, int32_t* idx, const loki_desc* desc, void* stream) {
+int loki_topk(const float* scores, int k, int32_t* idx, float* sel_out, const loki_desc* desc,
+              void* stream) {
   Shape sh;
   int rc = check_desc(desc, &sh);
   if (rc) return rc;
@@ -348,16 +346,18 @@ int loki_topk(const float* scores, int k, int32_t* idx, const loki_desc* desc, v
   REQUIRE_PTR(idx);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
   TopkParams tp{};
+  if (sel_out && !aligned16(sel_out)) return fail(LOKI_EINVAL, "sel_out is not 16-byte aligned");
   tp.scores = scores;
   tp.idx = idx;
+  tp.sel_scores = sel_out;
   tp.S = sh.S;
   tp.k = k;
   return hip_status(launch_topk(tp, sh.B * sh.Hq, (hipStream_t)stream), "topk");
 }
 
 int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
-                int k, float* out, const loki_desc* desc, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                const float* sel_scores, int k, float* out, const loki_desc* desc,
+                void* workspace, size_t workspace_bytes, void* stream) {
   Shape sh;
   int rc = check_desc(desc, &sh);
   if (rc) return rc;
@@ -372,14 +372,17 @@ int loki_attend(const float* qr, const void* kcache, const void* vcache, const i
   if (workspace_bytes < w.total)
     return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
   AttendParams ap{};
+  if (sel_scores && !aligned16(sel_scores))
+    return fail(LOKI_EINVAL, "sel_scores is not 16-byte aligned");
   ap.qr = qr;
   ap.kcache = kcache;
   ap.vcache = vcache;
   ap.idx = idx;
+  ap.sel_scores = sel_scores;
   ap.out = out;
   ap.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part);
   ap.k = k;
-  ap.d = sh.D;
+  ap.d = sel_scores ? sh.dp : sh.D;
   ap.nsplit = w.nsplit;
   ap.kc = kAttendChunk;
   ap.scale_log2 = scale_log2(desc);

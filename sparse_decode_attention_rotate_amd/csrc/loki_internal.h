@@ -57,6 +57,18 @@ struct AttendParams {
   Shape sh;
 };
 
+struct FusedParams {
+  const void* q;        // [B,Hq,D]
+  const void* kcache;
+  const void* vcache;
+  const float* P;       // [Hkv,D,D]
+  float* out;           // [B,Hq,D]
+  int32_t* idx_out;     // [B,Hq,k] nullable
+  int k;
+  float scale_log2;
+  Shape sh;
+};
+
 struct LayoutParams {
   const void* src;
   void* dst;
@@ -70,6 +82,11 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st);
 hipError_t launch_attend(const AttendParams& p, hipStream_t st);
 hipError_t launch_layout(const LayoutParams& p, hipStream_t st);
+
+// One-launch decode step (rotation, scores, top-k, attention) for shapes whose
+// per-unit scores fit the workgroup's LDS budget.
+bool fused_supported(const Shape& sh, int d, int k);
+hipError_t launch_fused(const FusedParams& p, hipStream_t st);
 
 // Rows of the selected set processed by one attention workgroup.
 constexpr int kAttendChunk = 512;

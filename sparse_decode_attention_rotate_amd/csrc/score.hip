@@ -33,6 +33,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   const int tl = threadIdx.x / LPT;
   const int t0 = tile * TILE;
 
+  // the panel of this (b, kv): S_cap rows of LPT*16 bytes; tokens >= S read as zeros
+  const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
+                                 head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
+                             (uint32_t)((size_t)sh.S_cap * LPT * 16));
+  u32x4 x[kScoreIters];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; it++) {
+    const int t = t0 + it * TPP + tl;
+    x[it] = load16(prs, t < sh.S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+  }
+
+  // qr slices (issued after the panel loads so both are in flight)
   float qv[G][E];
 #pragma unroll
   for (int h = 0; h < G; h++) {
@@ -43,17 +55,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       const float v = qrow[j];
       qv[h][e] = (j < p.d) ? v : 0.f;
     }
-  }
-
-  // the panel of this (b, kv): S_cap rows of LPT*16 bytes; tokens >= S read as zeros
-  const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
-                                 head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
-                             (uint32_t)((size_t)sh.S_cap * LPT * 16));
-  u32x4 x[kScoreIters];
-#pragma unroll
-  for (int it = 0; it < kScoreIters; it++) {
-    const int t = t0 + it * TPP + tl;
-    x[it] = load16(prs, t < sh.S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
   }
 
   float* srow = p.scores + ((size_t)b * sh.Hq + (size_t)kv * G) * sh.S;

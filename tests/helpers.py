@@ -66,11 +66,14 @@ def upload(wl: W.Workload, x: dict, dp: int = 32):
     return dev
 
 
-def run_decode(wl: W.Workload, dev: dict, d: int = None, k: int = None):
+def run_decode(wl: W.Workload, dev: dict, d: int = None, k: int = None, separate=False):
+    """One decode step; separate=True forces the per-phase launches."""
     d = wl.d if d is None else d
     k = wl.k if k is None else k
     loki = _loki()
     desc = dev["desc"]
+    if separate:
+        desc = desc.with_flags(loki.FLAG_SEPARATE_KERNELS)
     idx = torch.full((wl.B, wl.Hq, k), -7, dtype=torch.int32, device="cuda")
     if wl.append:
         out = loki.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"], dev["v"],

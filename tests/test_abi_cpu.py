@@ -115,9 +115,9 @@ def test_other_entry_points_validate(L):
     assert lib.loki_rotate_query(fake, None, fake, cd, None) == -1
     assert lib.loki_score(fake, fake, 0, fake, cd, None) == -1
     assert lib.loki_score(fake, fake, 129, fake, cd, None) == -1
-    assert lib.loki_topk(fake, 0, fake, cd, None) == -1
-    assert lib.loki_topk(fake, 101, fake, cd, None) == -1
-    assert lib.loki_attend(fake, fake, fake, fake, 10, fake, cd, fake, 8, None) == -3
+    assert lib.loki_topk(fake, 0, fake, None, cd, None) == -1
+    assert lib.loki_topk(fake, 101, fake, None, cd, None) == -1
+    assert lib.loki_attend(fake, fake, fake, fake, None, 10, fake, cd, fake, 8, None) == -3
     assert lib.loki_pack_kcache(fake, 129, fake, cd, None) == -1
     assert lib.loki_unpack_kcache(fake, -1, fake, cd, None) == -1
     assert lib.loki_decode_append(fake, None, fake, fake, fake, fake, 32, 10, fake, None, cd,

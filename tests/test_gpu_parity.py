@@ -150,6 +150,13 @@ def _topk_cases():
     hh[:, g.choice(32768, 655, replace=False)] *= 16.0
     cases.append(("heavy", hh, 4096))
     cases.append(("tiny-range", (1.0 + g.integers(0, 4, (2, 5000)) * 2.0 ** -23).astype(np.float32), 1234))
+    # exact duplicates of the k-th value scattered before and after it
+    dup = g.standard_normal((3, 4096)).astype(np.float32)
+    for row in dup:
+        kth = np.sort(row)[::-1][511]
+        row[g.choice(4096, 6, replace=False)] = kth
+    cases.append(("dup-at-threshold", dup, 512))
+    cases.append(("dup-at-threshold-16k", np.tile(dup[:, :4096], (1, 4)) * 1.0, 2048))
     return cases
 
 
@@ -163,6 +170,21 @@ def test_topk_bit_exact(L, name, s, k):
     idx = L.topk(sd, k, desc).cpu().numpy()[0]
     ref = oracle.topk_rows(s.astype(np.float64), k)
     assert np.array_equal(idx, ref)
+
+
+def test_topk_selected_scores_out(L):
+    g = np.random.default_rng(11)
+    s = g.standard_normal((4, 3000)).astype(np.float32)
+    s[:, 5] = -0.0
+    desc = L.Desc(batch=2, n_q_heads=2, n_kv_heads=2, head_dim=128, seq_len=3000,
+                  seq_capacity=3000, panel_dim=32, dtype=L.F16)
+    sd = torch.from_numpy(s).cuda().reshape(2, 2, 3000)
+    sel = torch.empty((2, 2, 700), dtype=torch.float32, device="cuda")
+    idx = L.topk(sd, 700, desc, sel_out=sel).cpu().numpy().reshape(4, 700)
+    got = sel.cpu().numpy().reshape(4, 700)
+    ref = np.take_along_axis(s, idx, axis=1)
+    ref[ref == 0] = 0.0
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 # --------------------------------------------------------- attention alone
@@ -182,6 +204,26 @@ def test_attend_given_index_sets(L, dtype, D, k, g):
     out = L.attend(qr, dev["kcache"], dev["v"], torch.from_numpy(idx).cuda(), dev["desc"])
     out = out.cpu().numpy().astype(np.float64)
     ref = oracle.attend_given(x["q"], x["krot"], x["v"], x["P"], idx, dtype)
+    err = H.rel_err_rows(out, ref)
+    H.log(f"  max rel err {err.max():.2e}")
+    assert err.max() < H.OUT_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_attend_with_low_dim_partial_logits(L, dtype):
+    """Per-step pipeline score -> topk (sel_out) -> attend(sel_scores): only the
+    key coordinates beyond the panel are read, same result."""
+    wl = _small(dtype, S=2000, k=250, tau=20.0 if dtype == "f32" else 40.0)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    desc = dev["desc"]
+    qr = L.rotate_query(dev["q"], dev["P"], desc)
+    sc = L.score(qr, dev["kcache"], 32, desc)
+    sel = torch.empty((wl.B, wl.Hq, 250), dtype=torch.float32, device="cuda")
+    idx = L.topk(sc, 250, desc, sel_out=sel)
+    out = L.attend(qr, dev["kcache"], dev["v"], idx, desc, sel_scores=sel)
+    out = out.cpu().numpy().astype(np.float64)
+    ref = oracle.attend_given(x["q"], x["krot"], x["v"], x["P"], idx.cpu().numpy(), dtype)
     err = H.rel_err_rows(out, ref)
     H.log(f"  max rel err {err.max():.2e}")
     assert err.max() < H.OUT_TOL[dtype]
@@ -227,15 +269,31 @@ E2E = {
 }
 
 
+@pytest.mark.parametrize("separate", [False, True], ids=["default", "separate"])
 @pytest.mark.parametrize("case", list(E2E), ids=list(E2E))
-def test_decode_end_to_end(L, case):
+def test_decode_end_to_end(L, case, separate):
     wl = _small(**E2E[case])
-    H.log(f"decode {case}: {W.describe(wl)}")
     x = W.generate(wl)
     dev = H.upload(wl, x)
-    out, idx = H.run_decode(wl, dev)
+    plan = L.decode_plan(dev["desc"], wl.d, wl.k, wl.append)
+    H.log(f"decode {case} separate={separate} one_launch={plan}: {W.describe(wl)}")
+    out, idx = H.run_decode(wl, dev, separate=separate)
     res = H.full_parity(wl, x, out, idx)
     H.log(f"  {res}")
+
+
+def test_launch_plan(L):
+    """Which workloads take the one-launch kernel."""
+    expect = {"single_head_f32": True, "llama2_7b_f16": True, "llama2_13b_f16": True,
+              "long_context_bf16": False, "gqa_llama3_8b_bf16": False}
+    for name, one in expect.items():
+        wl = W.get(name)
+        desc = H.make_desc(wl, 32)
+        assert L.decode_plan(desc, wl.d, wl.k, wl.append) == one, name
+        assert not L.decode_plan(desc.with_flags(L.FLAG_SEPARATE_KERNELS), wl.d, wl.k)
+    wl = _small("f16", S=3000, k=300)
+    assert not L.decode_plan(H.make_desc(wl, 32), 20, 300)      # d != dp
+    assert not L.decode_plan(H.make_desc(wl, 32), 32, 300, True)  # append
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -289,10 +347,17 @@ def test_workload_full_size(L, name):
     H.log(f"workload {name}: generating")
     x = W.generate(wl)
     dev = H.upload(wl, x)
-    H.log(f"workload {name}: decode on GPU")
+    H.log(f"workload {name}: decode on GPU (one launch: "
+          f"{L.decode_plan(dev['desc'], wl.d, wl.k, wl.append)})")
     out, idx = H.run_decode(wl, dev)
+    outs, idxs = None, None
+    if not wl.append:  # the appending workload would append twice
+        outs, idxs = H.run_decode(wl, dev, separate=True)
     del dev
     torch.cuda.empty_cache()
     H.log(f"workload {name}: oracle")
     res = H.full_parity(wl, x, out, idx)
     H.log(f"  {name}: {res}")
+    if outs is not None:
+        res = H.full_parity(wl, x, outs, idxs)
+        H.log(f"  {name} (separate launches): {res}")
