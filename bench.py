@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="after the run, 5 plain device-to-device copies of MB megabytes "
+                         "(reference for the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -250,6 +253,15 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
 
     print(json.dumps(result), flush=True)
 

@@ -22,7 +22,7 @@
 
 namespace loki {
 
-constexpr int kRowsPerBatch = 4;  // rows per lane group per load batch
+constexpr int kRowsPerBatch = 4;  // default rows per lane group per load batch
 
 template <int DT, int D, int NT>
 struct AttendGeom {
@@ -45,7 +45,7 @@ struct AttendSmem {
 // head: flattened (b, kv) of the caches.  On return thread tid < D holds the
 // merged (M, L, A) with A the unnormalised output coordinate tid, in the log2
 // domain: out[tid] = A / L.
-template <int DT, int D, int NT, bool SPLIT>
+template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch>
 __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2,
                                              const int* sidx, const float* slow, int nr,
                                              const void* kcache, const void* vcache,
@@ -54,7 +54,6 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
                                              float& L_out, float& A_out) {
   using G = AttendGeom<DT, D, NT>;
   constexpr int EB = G::EB, E = G::E, LPR = G::LPR, RPI = G::RPI, NG = G::NG;
-  constexpr int RB = kRowsPerBatch;
   constexpr int ROWS_PER_ITER = 2 * RB * NG;  // two batches in flight
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -7,10 +7,14 @@
 //
 // One launch, no intermediate buffers in HBM: per unit (b, kv) with its g
 // query heads,
-//  0. the query rows are rotated by P[kv] (P read from L2, coalesced columns,
-//     partial sums over row chunks merged in LDS);
+//  0. the panel coordinates of the query rows are rotated by P[kv] (16-byte
+//     loads of P's leading dp columns, partial sums reduced across lanes and
+//     waves) while the first two panel batches are already in flight;
 //  1. the contiguous leading-dp panel of the unit's keys is streamed with
-//     16-byte loads, two batches in flight, and the g score rows kept in LDS;
+//     16-byte loads, two batches in flight, the g score rows kept in LDS and
+//     their min / max folded on the way;
+//  0'. the loads for the remaining D-dp coordinates of the rotation are issued
+//     and stay in flight through the top-k;
 //  2. block_select (select_core.h) picks each head's top k from LDS;
 //  3. block_attend (attend_core.h) gathers the selected key tails and value
 //     rows and writes the output rows.
@@ -29,35 +33,61 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedKreg = 16;            // S <= 256 * 16
 constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per batch
 constexpr size_t kFusedDynBytes = 36 * 1024;
+#ifndef LOKI_FUSED_RB
+#define LOKI_FUSED_RB 4
+#endif
+constexpr int kFusedRowsPerBatch = LOKI_FUSED_RB;  // gather rows per lane group per batch
 
 template <int DT, int D, int LPT, int G>
-__global__ __launch_bounds__(kFusedThreads) void fused_kernel(FusedParams p) {
+__global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) {
   constexpr int NT = kFusedThreads;
   constexpr int NW = NT / 64;
   constexpr int E = Elem<DT>::kPerVec;
-  constexpr int TPP = NT / LPT;           // tokens per pass over the panel
-  constexpr int RG = NT / D;              // row chunks of the rotation
+  constexpr int DP = LPT * 16 / Elem<DT>::kBytes;  // panel width (== d)
+  constexpr int TPP = NT / LPT;                    // tokens per pass over the panel
   constexpr int NB = kFusedBatch;
+  // rotation of the panel coordinates: thread = (column quad, row slot)
+  constexpr int NQL = DP / 4, RSL = NT / NQL, NL = D / RSL;
+  // rotation of the remaining coordinates: 32 quad slots x 8 row slots
+  constexpr int NQR = (D - DP) / 4, RSR = NT / 32, NR = D / RSR;
+  static_assert(NT % NQL == 0 && D % RSL == 0 && NQR <= 32 && D % RSR == 0, "rotation tiling");
 
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SelectSmem<NW> ssm;
   __shared__ AttendSmem<DT, D, NT> asm_;
-  __shared__ float xq[G][D];       // query rows, fp32
-  __shared__ float qpart[RG][G][D];
-  __shared__ float qs[G][D];       // rotated query rows
+  __shared__ float xq[G][D];             // query rows, fp32
+  __shared__ float qpart[NW][G][D];      // per-wave partial rotations
+  __shared__ float qs[G][D];             // rotated query rows
+  __shared__ float rng[2][NW][G];        // per-wave score min / max
 
   const Shape& sh = p.sh;
   const int S = sh.S, k = p.k;
-  float* sc = reinterpret_cast<float*>(dyn);        // [G][S]
-  int* sidx = reinterpret_cast<int*>(sc + G * S);   // [G][k]
+  float* sc = reinterpret_cast<float*>(dyn);             // [G][S]
+  int* sidx = reinterpret_cast<int*>(sc + G * S);        // [G][k]
   float* slow = reinterpret_cast<float*>(sidx + G * k);  // [G][k]
 
   const size_t head = blockIdx.x;  // b * Hkv + kv
   const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query head of the group
 
-  // ---- 1a. first panel batch in flight before anything else
+  // ---- 0. rotation of the panel coordinates: qs[h][0:DP] = q[h] . P[kv][:, 0:DP]
+  // Its loads go out first: a wave's loads complete in issue order, so the
+  // panel loads issued after them do not delay the rotation.
+  const Rsrc Prs = make_rsrc(p.P + (size_t)kv * D * D, (uint32_t)(D * D * 4));
+  const int cql = tid % NQL, rsl = tid / NQL;
+  u32x4 pl[NL];
+#pragma unroll
+  for (int u = 0; u < NL; u++) pl[u] = load16(Prs, ((rsl + RSL * u) * D + 4 * cql) * 4);
+  float xv[(G * D + NT - 1) / NT];
+#pragma unroll
+  for (int u = 0; u < (G * D + NT - 1) / NT; u++) {
+    const int e = min(tid + u * NT, G * D - 1);  // clamped: the load needs no branch
+    xv[u] = load_elem<DT>(p.q, q0 * D + e);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the panel loads
+
+  // ---- 1a. two panel batches in flight during the rotation
   const int c = tid % LPT, tl = tid / LPT;
   const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
                                  head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
@@ -72,45 +102,64 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(FusedParams p) {
   };
   u32x4 xa[NB], xb[NB];
   issue(xa, 0);
+  issue(xb, NB);
 
-  // ---- 0. rotation of the g query rows: qs[h] = q[h] . P[kv]
-  for (int e = tid; e < G * D; e += NT)
-    xq[e / D][e % D] = load_elem<DT>(p.q, q0 * D + e);
-  __syncthreads();
-  {
-    // thread (j, rg) loads its D/RG entries of column j of P[kv] at once
-    constexpr int NI = D / RG;
-    const int j = tid % D, rg = tid / D;
-    const float* Pk = p.P + (size_t)kv * D * D + (size_t)rg * NI * D + j;
-    float pv[NI];
 #pragma unroll
-    for (int u = 0; u < NI; u++) pv[u] = Pk[(size_t)u * D];
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) acc[h] = 0.f;
-#pragma unroll
-    for (int u = 0; u < NI; u++)
-#pragma unroll
-      for (int h = 0; h < G; h++) acc[h] = fmaf(xq[h][rg * NI + u], pv[u], acc[h]);
-#pragma unroll
-    for (int h = 0; h < G; h++) qpart[rg][h][j] = acc[h];
+  for (int u = 0; u < (G * D + NT - 1) / NT; u++) {
+    const int e = tid + u * NT;
+    if (e < G * D) xq[e / D][e % D] = xv[u];
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += NT) {
-    float s = 0.f;
-#pragma unroll
-    for (int r = 0; r < RG; r++) s += qpart[r][e / D][e % D];
-    qs[e / D][e % D] = s;
-  }
-  __syncthreads();
-
-  // ---- 1b. low-dim scores of every token into LDS
   {
-    float qv[G][E];
+    float a[G][4];
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
-      for (int e = 0; e < E; e++) qv[h][e] = qs[h][c * E + e];  // c*E < dp == d
+      for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NL; u++) {
+      float f[4];
+      unpack16<F32>(pl[u], f);
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        const float x = xq[h][rsl + RSL * u];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
+      }
+    }
+    // lanes of one column quad are NQL apart within the wave
+#pragma unroll
+    for (int o = NQL; o < 64; o <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], o, 64);
+    if (lane < NQL)
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) qpart[wave][h][4 * cql + cc] = a[h][cc];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * DP; e += NT) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) s += qpart[w][e / DP][e % DP];
+    qs[e / DP][e % DP] = s;
+  }
+  __syncthreads();
+
+  // ---- 1b. low-dim scores of every token into LDS (and their range)
+  float lo[G], hi[G];
+  {
+    float qv[G][E];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      lo[h] = INFINITY;
+      hi[h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < E; e++) qv[h][e] = qs[h][c * E + e];  // c*E < DP == d
+    }
     auto consume = [&](const u32x4 (&x)[NB], int pass0) {
 #pragma unroll
       for (int it = 0; it < NB; it++) {
@@ -123,31 +172,97 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(FusedParams p) {
 #pragma unroll
           for (int e = 0; e < E; e++) a = fmaf(qv[h][e], f[e], a);
           a = group_sum<LPT>(a);
-          if (t < S && c == (h % LPT)) sc[h * S + t] = a;
+          if (t < S) {
+            lo[h] = fminf(lo[h], a);
+            hi[h] = fmaxf(hi[h], a);
+            if (c == (h % LPT)) sc[h * S + t] = a;
+          }
         }
       }
     };
     for (int pass = 0; pass < n_pass; pass += 2 * NB) {
-      issue(xb, pass + NB);
       consume(xa, pass);
       if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
       consume(xb, pass + NB);
+      if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
     }
   }
+#pragma unroll
+  for (int h = 0; h < G; h++) {
+    lo[h] = -wave_max(-lo[h]);
+    hi[h] = wave_max(hi[h]);
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      rng[0][wave][h] = lo[h];
+      rng[1][wave][h] = hi[h];
+    }
+
+  // ---- 0'. the rest of the rotation: its P loads stay in flight through the top-k
+  const int cqr = tid % 32, rsr = tid / 32;
+  u32x4 pr[NR];
+#pragma unroll
+  for (int u = 0; u < NR; u++)
+    pr[u] = load16(Prs, cqr < NQR ? ((rsr + RSR * u) * D + DP + 4 * cqr) * 4 : kOutOfRange);
   __syncthreads();
 
   // ---- 2. top-k of each head's scores, from LDS
   for (int h = 0; h < G; h++) {
+    float l0 = rng[0][0][h], h0 = rng[1][0][h];
+#pragma unroll
+    for (int w = 1; w < NW; w++) {
+      l0 = fminf(l0, rng[0][w][h]);
+      h0 = fmaxf(h0, rng[1][w][h]);
+    }
     const float* row = sc + h * S;
     auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
-    block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm);
+    block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0, h0);
     __syncthreads();
   }
+
+  // ---- 0''. finish the rotation: qs[h][DP:D]
+  {
+    float a[G][4];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NR; u++) {
+      float f[4];
+      unpack16<F32>(pr[u], f);
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        const float x = xq[h][rsr + RSR * u];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], 32, 64);
+    if (lane < 32 && cqr < NQR)
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) qpart[wave][h][DP + 4 * cqr + cc] = a[h][cc];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * (D - DP); e += NT) {
+    const int h = e / (D - DP), j = DP + e % (D - DP);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) s += qpart[w][h][j];
+    qs[h][j] = s;
+  }
+  __syncthreads();
 
   // ---- 3. exact attention over the selected tokens of each head
   for (int h = 0; h < G; h++) {
     float M, L, A;
-    block_attend<DT, D, NT, true>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
+    block_attend<DT, D, NT, true, kFusedRowsPerBatch>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
                                   p.kcache, p.vcache, head, sh, asm_, M, L, A);
     if (tid < D) p.out[(q0 + h) * D + tid] = A / L;
     if (p.idx_out)

@@ -63,10 +63,13 @@ struct SelectSmem {
 // All NT threads of the workgroup call this together.  load_score(i) returns
 // score i for 0 <= i < S and is harmless (any value) for i >= S.  Writes the
 // k selected indices, ascending, to out_idx and their scores to out_val
-// (nullable); both may point to global memory or LDS.
+// (nullable); both may point to global memory or LDS.  With have_range the
+// caller passes the row's exact minimum and maximum (saves one pass).
 template <int NT, int KREG, typename Load>
 __device__ __forceinline__ void block_select(Load load_score, int S, int k, int32_t* out_idx,
-                                             float* out_val, SelectSmem<NT / 64>& sm) {
+                                             float* out_val, SelectSmem<NT / 64>& sm,
+                                             bool have_range = false, float lo_in = 0.f,
+                                             float hi_in = 0.f) {
   constexpr int NW = NT / 64;
   constexpr int PER_WAVE = KREG * 64;  // contiguous indices owned by one wave
   constexpr int BPL = kBins / NW / 64;  // bins per lane in the scan
@@ -100,26 +103,32 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
   // ---- range of the row
   for (int e = tid; e < kBins; e += NT) sm.hist[e] = 0u;
   if (tid == 0) sm.n_cand = 0;
-  float lo = INFINITY, hi = -INFINITY;
-  each([&](int, int i, float v) {
-    if (i < S) {
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
+  float lo = lo_in, hi = hi_in;
+  if (!have_range) {
+    lo = INFINITY;
+    hi = -INFINITY;
+    each([&](int, int i, float v) {
+      if (i < S) {
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+    });
+    lo = -wave_max(-lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      sm.wmin[wave] = lo;
+      sm.wmax[wave] = hi;
     }
-  });
-  lo = -wave_max(-lo);
-  hi = wave_max(hi);
-  if (lane == 0) {
-    sm.wmin[wave] = lo;
-    sm.wmax[wave] = hi;
   }
   __syncthreads();
-  lo = sm.wmin[0];
-  hi = sm.wmax[0];
+  if (!have_range) {
+    lo = sm.wmin[0];
+    hi = sm.wmax[0];
 #pragma unroll
-  for (int w = 1; w < NW; w++) {
-    lo = fminf(lo, sm.wmin[w]);
-    hi = fmaxf(hi, sm.wmax[w]);
+    for (int w = 1; w < NW; w++) {
+      lo = fminf(lo, sm.wmin[w]);
+      hi = fmaxf(hi, sm.wmax[w]);
+    }
   }
   const float range = hi - lo;
   float scale = (range > 0.f && range < INFINITY) ? (float)(kBins - 1) / range : 0.f;
