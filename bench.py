@@ -59,16 +59,19 @@ def src_sha(name):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel, per_launch_alg_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current source of that kernel; else None."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic_<workload>.txt, lines "traffic {json}"), if
+    the counters were taken on the current source of that kernel; else None."""
+    p = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
     if not os.path.exists(p):
         return None
-    t = json.load(open(p))
-    if t.get("src_sha") != src_sha(KERNEL_SOURCES[kernel]):
-        return None
-    return t.get("hbm_bytes_per_launch")
+    for line in open(p):
+        if line.startswith("traffic "):
+            t = json.loads(line[len("traffic "):])
+            if t.get("kernel") == kernel and t.get("src_sha") == src_sha(KERNEL_SOURCES[kernel]):
+                return t.get("hbm_bytes_per_launch")
+    return None
 
 
 def main():
@@ -221,7 +224,7 @@ def main():
         dom_us, dom_bytes = per_kernel[dom], per_kernel_bytes[dom]
         kernels = per_kernel
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name, dom, dom_bytes)
+    traffic = measured_traffic(wl.name, dom)
 
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
