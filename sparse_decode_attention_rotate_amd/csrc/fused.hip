@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
     const int e = tid + u * NT;
     if (e < G * D) xq[e / D][e % D] = xv[u];
   }
+  if (G == 1) select_clear<NT>(ssm);  // the histogram fills while scoring
   __syncthreads();
   {
     float a[G][4];
@@ -149,8 +150,13 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   }
   __syncthreads();
 
-  // ---- 1b. low-dim scores of every token into LDS (and their range)
+  // ---- 1b. low-dim scores of every token into LDS.  Single head: the
+  // scores of the first batch fix a provisional binning range, the select
+  // histogram is built as the remaining scores are produced (clamped linear
+  // bins stay monotone, whatever the range).  Several heads: the exact range
+  // is tracked and the histograms are built after scoring.
   float lo[G], hi[G];
+  float blo = 0.f, bscale = 0.f;  // binning of the single-head histogram
   {
     float qv[G][E];
 #pragma unroll
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
 #pragma unroll
       for (int e = 0; e < E; e++) qv[h][e] = qs[h][c * E + e];  // c*E < DP == d
     }
-    auto consume = [&](const u32x4 (&x)[NB], int pass0) {
+    auto consume = [&](const u32x4 (&x)[NB], int pass0, bool hist) {
 #pragma unroll
       for (int it = 0; it < NB; it++) {
         float f[E];
@@ -175,29 +181,57 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
           if (t < S) {
             lo[h] = fminf(lo[h], a);
             hi[h] = fmaxf(hi[h], a);
-            if (c == (h % LPT)) sc[h * S + t] = a;
+            if (c == (h % LPT)) {
+              sc[h * S + t] = a;
+              if (G == 1 && hist) atomicAdd(&ssm.hist[lin_bin(a, blo, bscale)], 1u);
+            }
           }
         }
       }
     };
-    for (int pass = 0; pass < n_pass; pass += 2 * NB) {
-      consume(xa, pass);
+    consume(xa, 0, false);
+    if (G == 1) {
+      // provisional range from the first batch of scores, then their histogram
+      const float l0 = -wave_max(-lo[0]), h0 = wave_max(hi[0]);
+      if (lane == 0) {
+        rng[0][wave][0] = l0;
+        rng[1][wave][0] = h0;
+      }
+      __syncthreads();
+      blo = rng[0][0][0];
+      float bhi = rng[1][0][0];
+#pragma unroll
+      for (int w = 1; w < NW; w++) {
+        blo = fminf(blo, rng[0][w][0]);
+        bhi = fmaxf(bhi, rng[1][w][0]);
+      }
+      bscale = bin_scale(blo, bhi);
+      for (int t = tid; t < min(S, NB * TPP); t += NT)
+        atomicAdd(&ssm.hist[lin_bin(sc[t], blo, bscale)], 1u);
+    }
+    if (2 * NB < n_pass) issue(xa, 2 * NB);
+    consume(xb, NB, true);
+    if (3 * NB < n_pass) issue(xb, 3 * NB);
+    for (int pass = 2 * NB; pass < n_pass; pass += 2 * NB) {
+      consume(xa, pass, true);
       if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
-      consume(xb, pass + NB);
+      consume(xb, pass + NB, true);
       if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
     }
   }
-#pragma unroll
-  for (int h = 0; h < G; h++) {
-    lo[h] = -wave_max(-lo[h]);
-    hi[h] = wave_max(hi[h]);
-  }
-  if (lane == 0)
+  if (G > 1) {
 #pragma unroll
     for (int h = 0; h < G; h++) {
-      rng[0][wave][h] = lo[h];
-      rng[1][wave][h] = hi[h];
+      lo[h] = -wave_max(-lo[h]);
+      hi[h] = wave_max(hi[h]);
     }
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        rng[0][wave][h] = lo[h];
+        rng[1][wave][h] = hi[h];
+      }
+  }
 
   // ---- 0'. the rest of the rotation: its P loads stay in flight through the top-k
   const int cqr = tid % 32, rsr = tid / 32;
@@ -208,17 +242,25 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   __syncthreads();
 
   // ---- 2. top-k of each head's scores, from LDS
-  for (int h = 0; h < G; h++) {
-    float l0 = rng[0][0][h], h0 = rng[1][0][h];
-#pragma unroll
-    for (int w = 1; w < NW; w++) {
-      l0 = fminf(l0, rng[0][w][h]);
-      h0 = fmaxf(h0, rng[1][w][h]);
-    }
-    const float* row = sc + h * S;
-    auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
-    block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0, h0);
+  if (G == 1) {
+    auto load_score = [&](int i) -> float { return i < S ? sc[i] : 0.f; };
+    RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
+    select_from_histogram<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale);
     __syncthreads();
+  } else {
+    for (int h = 0; h < G; h++) {
+      float l0 = rng[0][0][h], h0 = rng[1][0][h];
+#pragma unroll
+      for (int w = 1; w < NW; w++) {
+        l0 = fminf(l0, rng[0][w][h]);
+        h0 = fmaxf(h0, rng[1][w][h]);
+      }
+      const float* row = sc + h * S;
+      auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
+      block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0,
+                                   h0);
+      __syncthreads();
+    }
   }
 
   // ---- 0''. finish the rotation: qs[h][DP:D]

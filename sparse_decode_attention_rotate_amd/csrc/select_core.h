@@ -5,24 +5,25 @@
 // tokens of the KV-cache are ranked by their low-dimensional scores and only
 // the top k are kept for the exact attention.
 //
-// Exact selection in one workgroup per row of S scores, rule (score
-// descending, index ascending), output in ascending index order:
-//  1. Linear binning.  bin(s) = floor((s - min) * 2047 / (max - min)) is a
-//     non-decreasing function of s, so every score in a higher bin exceeds
-//     every score in a lower one.  One LDS histogram of 2048 bins (spread
-//     data, few atomic collisions) and a DPP prefix scan over the bins in
-//     descending order give the bin b* that holds the k-th largest score.
-//  2. Exact threshold inside b*.  With few members (<= 64) one wave ranks
-//     them by (key, index) and reads off the threshold key T and the number r
-//     of keys equal to T that are taken.  Otherwise (skewed rows) radix passes
-//     over 8-bit digits of the members' order-preserving keys, per-wave LDS
-//     histograms, early stop once a digit group is taken whole.
-//  3. Ordered compaction: select key > T, or key == T among the first r such
-//     indices.  Each wave owns a contiguous index range: counts by ballot, one
-//     barrier to exchange them, then each wave writes its indices at offsets
-//     from ballot + mbcnt ranks.
-// Scores stay in registers when S <= threads * KREG, else they are re-read
-// (from L2: the row was just written) in each step.
+// Exact selection of the k elements of a row of S scores that rank first by
+// (score descending, index ascending); the indices come out ascending.
+//  1. Linear binning.  bin(s) = clamp(floor((s - lo) * scale), 0, 2047) is a
+//     non-decreasing function of s for ANY lo and scale >= 0, so every score
+//     in a higher bin exceeds every score in a lower one.  One LDS histogram
+//     of 2048 bins (few atomic collisions on spread data) and a DPP prefix
+//     scan over the bins in descending order give the bin b* that holds the
+//     k-th largest score.  lo and scale come from the row's range or, in the
+//     fused kernel, from a first batch of scores (the histogram is then built
+//     while scoring; clamping keeps the binning monotone).
+//  2. The last taken element.  Elements are ordered by (order-preserving key
+//     descending, index ascending); the k-th one, (T, I), is found inside b*:
+//     with few members one wave ranks them; otherwise radix passes over 8-bit
+//     digits of the members' keys (per-wave LDS histograms), then the
+//     position of the last taken key among equal keys.
+//  3. Ordered compaction: element i is taken iff key > T or (key == T and
+//     i <= I).  Each wave owns a contiguous index range: counts by ballot, one
+//     barrier, then each wave writes its indices at offsets from mbcnt ranks.
+// Scores stay in registers when S <= threads * KREG, else they are re-read.
 #pragma once
 
 #include <limits.h>
@@ -45,7 +46,15 @@ __device__ __forceinline__ int lin_bin(float s, float lo, float scale) {
   return b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
 }
 
-// LDS scratch of one block_select call.
+// scale of the linear binning of [lo, hi]; 0 (one bin) when the range is empty,
+// not finite or too small to scale
+__device__ __forceinline__ float bin_scale(float lo, float hi) {
+  const float range = hi - lo;
+  float scale = (range > 0.f && range < INFINITY) ? (float)(kBins - 1) / range : 0.f;
+  return scale < INFINITY ? scale : 0.f;
+}
+
+// LDS scratch of one selection.
 template <int NW>
 struct SelectSmem {
   unsigned hist[kBins];
@@ -56,91 +65,71 @@ struct SelectSmem {
   unsigned cand_key[kFewCandidates];
   int cand_idx[kFewCandidates];
   unsigned thr_key, r_digit, r_gt, r_eq;
-  int thr_take;
-  int wcnt[NW][2];
+  int thr_idx;
+  int wcnt[NW];
 };
 
-// All NT threads of the workgroup call this together.  load_score(i) returns
-// score i for 0 <= i < S and is harmless (any value) for i >= S.  Writes the
-// k selected indices, ascending, to out_idx and their scores to out_val
-// (nullable); both may point to global memory or LDS.  With have_range the
-// caller passes the row's exact minimum and maximum (saves one pass).
+// Zero the histogram (all NT threads; a barrier must follow before use).
+template <int NT, int NW>
+__device__ __forceinline__ void select_clear(SelectSmem<NW>& sm) {
+  for (int e = threadIdx.x; e < kBins; e += NT) sm.hist[e] = 0u;
+  if (threadIdx.x == 0) sm.n_cand = 0;
+}
+
+// A thread's share of a row of S scores: element j has index
+// wave*per_wave + j*64 + lane, so each wave owns a contiguous index range.
+// With KREG > 0 (S <= NT*KREG) the scores are loaded once into registers;
+// otherwise (KREG == 0) each pass re-reads them through load_score.
+// load_score(i) returns score i for i < S and any value for i >= S.
 template <int NT, int KREG, typename Load>
-__device__ __forceinline__ void block_select(Load load_score, int S, int k, int32_t* out_idx,
-                                             float* out_val, SelectSmem<NT / 64>& sm,
-                                             bool have_range = false, float lo_in = 0.f,
-                                             float hi_in = 0.f) {
+struct RowView {
+  static constexpr int NW = NT / 64;
+  static constexpr int NJ = KREG > 0 ? KREG : 1;
+  Load load_score;
+  int S, per_wave, nj, base;
+  float sv[NJ];
+
+  __device__ __forceinline__ RowView(Load l, int S_) : load_score(l), S(S_) {
+    per_wave = KREG > 0 ? KREG * 64 : (S + NW * 64 - 1) / (NW * 64) * 64;
+    nj = per_wave / 64;
+    base = (threadIdx.x >> 6) * per_wave + (threadIdx.x & 63);
+    if constexpr (KREG > 0) {
+#pragma unroll
+      for (int j = 0; j < KREG; j++) sv[j] = load_score(base + j * 64);
+    }
+  }
+
+  // f(i, v) for each element of this thread (i may be >= S: check i < S)
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) {
+    if constexpr (KREG > 0) {
+#pragma unroll
+      for (int j = 0; j < KREG; j++) f(base + j * 64, sv[j]);
+    } else {
+      for (int j = 0; j < nj; j++) {
+        const int i = base + j * 64;
+        f(i, load_score(i));
+      }
+    }
+  }
+};
+
+// Steps 1 (after the histogram) to 3.  sm.hist holds the histogram of the
+// row under (lo, scale).  All NT threads call it together.
+template <int NT, int KREG, typename Load>
+__device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& row, int k,
+                                                      int32_t* out_idx, float* out_val,
+                                                      SelectSmem<NT / 64>& sm, float lo,
+                                                      float scale) {
   constexpr int NW = NT / 64;
-  constexpr int PER_WAVE = KREG * 64;  // contiguous indices owned by one wave
   constexpr int BPL = kBins / NW / 64;  // bins per lane in the scan
   static_assert(BPL >= 1 && kBins % (NW * 64) == 0, "bins split over the waves");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = row.S;
+  auto each = [&](auto&& f) { row.each(f); };
 
-  // element j of this thread has index wave*per_wave + j*64 + lane: each wave
-  // owns a contiguous range of per_wave indices (KREG*64 with registers)
-  constexpr int NJ = KREG > 0 ? KREG : 1;
-  const int per_wave = KREG > 0 ? PER_WAVE : (S + NW * 64 - 1) / (NW * 64) * 64;
-  const int nj = per_wave / 64;
-  auto index_of = [&](int j) -> int { return wave * per_wave + j * 64 + lane; };
-  float sv[NJ];
-  if constexpr (KREG > 0) {
-#pragma unroll
-    for (int j = 0; j < KREG; j++) sv[j] = load_score(index_of(j));
-  }
-  // f(j, i, v) for every element of this thread (i may be >= S)
-  auto each = [&](auto&& f) {
-    if constexpr (KREG > 0) {
-#pragma unroll
-      for (int j = 0; j < KREG; j++) f(j, index_of(j), sv[j]);
-    } else {
-      for (int j = 0; j < nj; j++) {
-        const int i = index_of(j);
-        f(j, i, load_score(i));
-      }
-    }
-  };
-
-  // ---- range of the row
-  for (int e = tid; e < kBins; e += NT) sm.hist[e] = 0u;
-  if (tid == 0) sm.n_cand = 0;
-  float lo = lo_in, hi = hi_in;
-  if (!have_range) {
-    lo = INFINITY;
-    hi = -INFINITY;
-    each([&](int, int i, float v) {
-      if (i < S) {
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-      }
-    });
-    lo = -wave_max(-lo);
-    hi = wave_max(hi);
-    if (lane == 0) {
-      sm.wmin[wave] = lo;
-      sm.wmax[wave] = hi;
-    }
-  }
-  __syncthreads();
-  if (!have_range) {
-    lo = sm.wmin[0];
-    hi = sm.wmax[0];
-#pragma unroll
-    for (int w = 1; w < NW; w++) {
-      lo = fminf(lo, sm.wmin[w]);
-      hi = fmaxf(hi, sm.wmax[w]);
-    }
-  }
-  const float range = hi - lo;
-  float scale = (range > 0.f && range < INFINITY) ? (float)(kBins - 1) / range : 0.f;
-  if (!(scale < INFINITY)) scale = 0.f;  // subnormal range: everything in one bin
-
-  // ---- 1. linear-bin histogram and the bin of the k-th largest score
-  each([&](int, int i, float v) {
-    if (i < S) atomicAdd(&sm.hist[lin_bin(v, lo, scale)], 1u);
-  });
-  __syncthreads();
-  // descending scan: wave w covers positions [w*kBins/NW, (w+1)*kBins/NW),
-  // position q holds bin kBins-1-q, each lane BPL consecutive positions
+  // ---- 1b. descending scan over the bins: wave w covers positions
+  // [w*kBins/NW, (w+1)*kBins/NW), position q holds bin kBins-1-q
   unsigned c[BPL];
   unsigned tot = 0u;
 #pragma unroll
@@ -168,9 +157,9 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
   const int rem = k - sm.sel_gt;  // 1 <= rem <= members of b*
   const int nb = sm.sel_eq;
 
-  // ---- 2. exact threshold key inside b*
+  // ---- 2. the last taken element (T, I) inside b*
   if (nb <= kFewCandidates) {
-    each([&](int, int i, float v) {
+    each([&](int i, float v) {
       if (i < S && lin_bin(v, lo, scale) == bstar) {
         const int slot = atomicAdd(&sm.n_cand, 1);
         sm.cand_key[slot] = order_key(v);
@@ -188,23 +177,21 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
         const int oi = sm.cand_idx[m];
         rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
       }
-      const unsigned long long at = __ballot(mine && rank == rem - 1);  // one lane
-      const int src = at ? __ffsll((long long)at) - 1 : 0;
-      const unsigned T = (unsigned)__shfl((int)mk, src, 64);
-      const unsigned long long teq = __ballot(mine && mk == T && rank < rem);
-      if (lane == 0) {
-        sm.thr_key = T;
-        sm.thr_take = __popcll(teq);
+      if (mine && rank == rem - 1) {  // exactly one lane
+        sm.thr_key = mk;
+        sm.thr_idx = mi;
       }
     }
   } else {
+    // radix passes over the keys of b*'s members
     unsigned prefix = 0u, pmask = 0u;
     int rr = rem;
+    bool whole = false;
     for (int pass = 0; pass < 4; pass++) {
       const int shift = 24 - 8 * pass;
       for (int e = tid; e < NW * 256; e += NT) (&sm.whist[0][0])[e] = 0u;
       __syncthreads();
-      each([&](int, int i, float v) {
+      each([&](int i, float v) {
         if (i < S && lin_bin(v, lo, scale) == bstar) {
           const unsigned key = order_key(v);
           if ((key & pmask) == prefix) atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
@@ -239,13 +226,15 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
       rr -= (int)sm.r_gt;
       prefix |= sm.r_digit << shift;
       pmask |= 0xffu << shift;
-      const bool done = (int)sm.r_eq == rr;  // the whole prefix group is taken
+      whole = (int)sm.r_eq == rr;  // the whole prefix group is taken
       __syncthreads();
-      if (done) break;
+      if (whole) break;
     }
-    // T = smallest key of the taken prefix group: everything >= T is selected
+    // T: the smallest key of the taken prefix group (the exact key when all
+    // passes ran); I: every key equal to T is taken if the group was taken
+    // whole, else the rr-th one in index order
     unsigned tmin = 0xffffffffu;
-    each([&](int, int i, float v) {
+    each([&](int i, float v) {
       if (i < S && lin_bin(v, lo, scale) == bstar) {
         const unsigned key = order_key(v);
         if ((key & pmask) == prefix) tmin = min(tmin, key);
@@ -255,53 +244,103 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
     for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (unsigned)__shfl_xor((int)tmin, o, 64));
     if (lane == 0) sm.wtot[wave] = tmin;
     __syncthreads();
-    if (tid == 0) {
-      unsigned t = sm.wtot[0];
-      for (int w = 1; w < NW; w++) t = min(t, sm.wtot[w]);
-      sm.thr_key = t;
-      // all passes resolved: take rr of the keys equal to T; early stop: all of them
-      sm.thr_take = (pmask == 0xffffffffu) ? rr : INT_MAX;
+    unsigned T = sm.wtot[0];
+    for (int w = 1; w < NW; w++) T = min(T, sm.wtot[w]);
+    if (whole) {
+      if (tid == 0) {
+        sm.thr_key = T;
+        sm.thr_idx = INT_MAX;
+      }
+    } else {
+      // the rr-th index (ascending) among keys equal to T
+      int cnt = 0;
+      each([&](int i, float v) { cnt += __popcll(__ballot(i < S && order_key(v) == T)); });
+      if (lane == 0) sm.wcnt[wave] = cnt;
+      __syncthreads();
+      int seen = 0;
+      for (int w = 0; w < wave; w++) seen += sm.wcnt[w];
+      each([&](int i, float v) {
+        const bool eq = i < S && order_key(v) == T;
+        const unsigned long long be = __ballot(eq);
+        if (eq && seen + lane_rank(be) == rr - 1) {
+          sm.thr_key = T;
+          sm.thr_idx = i;
+        }
+        seen += __popcll(be);
+      });
     }
   }
   __syncthreads();
 
-  // ---- 3. ordered compaction
+  // ---- 3. ordered compaction: take key > T, or key == T with index <= I
   const unsigned T = sm.thr_key;
-  const int r = sm.thr_take;
-  int32_t* irow = out_idx;
-  float* vrow = out_val;
-  int gt_w = 0, eq_w = 0;
-  each([&](int, int i, float v) {
+  const int I = sm.thr_idx;
+  auto taken = [&](int i, float v) -> bool {
     const unsigned key = order_key(v);
-    gt_w += __popcll(__ballot(i < S && key > T));
-    eq_w += __popcll(__ballot(i < S && key == T));
-  });
-  if (lane == 0) {
-    sm.wcnt[wave][0] = gt_w;
-    sm.wcnt[wave][1] = eq_w;
-  }
+    return i < S && (key > T || (key == T && i <= I));
+  };
+  int cnt = 0;
+  each([&](int i, float v) { cnt += __popcll(__ballot(taken(i, v))); });
+  if (lane == 0) sm.wcnt[wave] = cnt;
   __syncthreads();
-  int out = 0, eq_seen = 0;
-  for (int w = 0; w < wave; w++) {
-    const int ce = sm.wcnt[w][1];
-    const int take = max(0, min(ce, r - eq_seen));
-    out += sm.wcnt[w][0] + take;
-    eq_seen += ce;
-  }
-  each([&](int, int i, float v) {
-    const unsigned key = order_key(v);
-    const bool gt = i < S && key > T, eq = i < S && key == T;
-    const unsigned long long be = __ballot(eq);
-    const bool sel = gt || (eq && eq_seen + lane_rank(be) < r);
+  int out = 0;
+  for (int w = 0; w < wave; w++) out += sm.wcnt[w];
+  each([&](int i, float v) {
+    const bool sel = taken(i, v);
     const unsigned long long bs = __ballot(sel);
     const int pos = out + lane_rank(bs);
-    if (sel && pos < k) {  // exactly k are selected; the bound only guards the row
-      irow[pos] = i;
-      if (vrow) vrow[pos] = v;
+    if (sel && pos < k) {  // exactly k are taken; the bound only guards the row
+      out_idx[pos] = i;
+      if (out_val) out_val[pos] = v == 0.f ? 0.f : v;  // -0 reported as +0
     }
     out += __popcll(bs);
-    eq_seen += __popcll(be);
   });
+}
+
+// Whole selection from the scores alone (range, histogram, steps 1-3).
+// With have_range the caller passes the row's minimum and maximum.
+template <int NT, int KREG, typename Load>
+__device__ __forceinline__ void block_select(Load load_score, int S, int k, int32_t* out_idx,
+                                             float* out_val, SelectSmem<NT / 64>& sm,
+                                             bool have_range = false, float lo_in = 0.f,
+                                             float hi_in = 0.f) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  RowView<NT, KREG, Load> row(load_score, S);
+  select_clear<NT>(sm);
+  float lo = lo_in, hi = hi_in;
+  if (!have_range) {
+    lo = INFINITY;
+    hi = -INFINITY;
+    row.each([&](int i, float v) {
+      if (i < S) {
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+    });
+    lo = -wave_max(-lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      sm.wmin[wave] = lo;
+      sm.wmax[wave] = hi;
+    }
+  }
+  __syncthreads();
+  if (!have_range) {
+    lo = sm.wmin[0];
+    hi = sm.wmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) {
+      lo = fminf(lo, sm.wmin[w]);
+      hi = fmaxf(hi, sm.wmax[w]);
+    }
+  }
+  const float scale = bin_scale(lo, hi);
+  row.each([&](int i, float v) {
+    if (i < S) atomicAdd(&sm.hist[lin_bin(v, lo, scale)], 1u);
+  });
+  __syncthreads();
+  select_from_histogram<NT, KREG>(row, k, out_idx, out_val, sm, lo, scale);
 }
 
 }  // namespace loki
