@@ -66,6 +66,11 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   int* sidx = reinterpret_cast<int*>(sc + G * S);        // [G][k]
   float* slow = reinterpret_cast<float*>(sidx + G * k);  // [G][k]
 
+  // Wave priority: the short latency-bound phases (rotation, top-k) run at
+  // high priority so that they are not starved of issue slots by the
+  // streaming phases of co-resident workgroups; streaming runs at the lowest.
+  __builtin_amdgcn_s_setprio(3);
+
   const size_t head = blockIdx.x;  // b * Hkv + kv
   const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   }
   __syncthreads();
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- 1b. low-dim scores of every token into LDS.  Single head: the
   // scores of the first batch fix a provisional binning range, the select
   // histogram is built as the remaining scores are produced (clamped linear
@@ -233,6 +239,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
       }
   }
 
+  __builtin_amdgcn_s_setprio(3);
   // ---- 0'. the rest of the rotation: its P loads stay in flight through the top-k
   const int cqr = tid % 32, rsr = tid / 32;
   u32x4 pr[NR];
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
 
   // ---- 2. top-k of each head's scores, from LDS
   if (G == 1) {
-    auto load_score = [&](int i) -> float { return i < S ? sc[i] : 0.f; };
+    auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
     RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
     select_from_histogram<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale);
     __syncthreads();
@@ -301,6 +308,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   }
   __syncthreads();
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- 3. exact attention over the selected tokens of each head
   for (int h = 0; h < G; h++) {
     float M, L, A;

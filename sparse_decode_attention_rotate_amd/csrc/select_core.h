@@ -17,13 +17,17 @@
 //     while scoring; clamping keeps the binning monotone).
 //  2. The last taken element.  Elements are ordered by (order-preserving key
 //     descending, index ascending); the k-th one, (T, I), is found inside b*:
-//     with few members one wave ranks them; otherwise radix passes over 8-bit
-//     digits of the members' keys (per-wave LDS histograms), then the
-//     position of the last taken key among equal keys.
+//     with few members (the common case) one pass over the row collects them
+//     and counts, per wave, the members of higher bins, then one wave ranks
+//     the candidates with lane reads; otherwise radix passes over 8-bit digits
+//     of the members' keys (per-wave LDS histograms), then the position of the
+//     last taken key among equal keys, then a counting pass.
 //  3. Ordered compaction: element i is taken iff key > T or (key == T and
-//     i <= I).  Each wave owns a contiguous index range: counts by ballot, one
-//     barrier, then each wave writes its indices at offsets from mbcnt ranks.
-// Scores stay in registers when S <= threads * KREG, else they are re-read.
+//     i <= I).  Each wave owns a contiguous index range whose taken count is
+//     known from step 2; each wave writes its indices at offsets from mbcnt
+//     ranks of its ballots.
+// Order keys stay in registers when S <= threads * KREG, else the scores are
+// re-read; padding elements (index >= S) are masked in every ballot.
 #pragma once
 
 #include <limits.h>
@@ -39,6 +43,11 @@ __device__ __forceinline__ unsigned order_key(float s) {
   unsigned u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key (a -0 score comes back as +0).
+__device__ __forceinline__ float key_score(unsigned key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 __device__ __forceinline__ int lin_bin(float s, float lo, float scale) {
@@ -76,18 +85,19 @@ __device__ __forceinline__ void select_clear(SelectSmem<NW>& sm) {
   if (threadIdx.x == 0) sm.n_cand = 0;
 }
 
-// A thread's share of a row of S scores: element j has index
+// A thread's share of a row of S scores, as order keys: element j has index
 // wave*per_wave + j*64 + lane, so each wave owns a contiguous index range.
-// With KREG > 0 (S <= NT*KREG) the scores are loaded once into registers;
-// otherwise (KREG == 0) each pass re-reads them through load_score.
-// load_score(i) returns score i for i < S and any value for i >= S.
+// With KREG > 0 (S <= NT*KREG) the keys are computed once and kept in
+// registers; otherwise (KREG == 0) each pass re-reads the scores through
+// load_score.  load_score(i) returns score i for i < S and any value for
+// i >= S: every use masks those elements with i < S.
 template <int NT, int KREG, typename Load>
 struct RowView {
   static constexpr int NW = NT / 64;
   static constexpr int NJ = KREG > 0 ? KREG : 1;
   Load load_score;
   int S, per_wave, nj, base;
-  float sv[NJ];
+  unsigned kv[NJ];
 
   __device__ __forceinline__ RowView(Load l, int S_) : load_score(l), S(S_) {
     per_wave = KREG > 0 ? KREG * 64 : (S + NW * 64 - 1) / (NW * 64) * 64;
@@ -95,27 +105,27 @@ struct RowView {
     base = (threadIdx.x >> 6) * per_wave + (threadIdx.x & 63);
     if constexpr (KREG > 0) {
 #pragma unroll
-      for (int j = 0; j < KREG; j++) sv[j] = load_score(base + j * 64);
+      for (int j = 0; j < KREG; j++) kv[j] = order_key(load_score(base + j * 64));
     }
   }
 
-  // f(i, v) for each element of this thread (i may be >= S: check i < S)
+  // f(i, key) for each element of this thread (i may be >= S)
   template <typename F>
   __device__ __forceinline__ void each(F&& f) {
     if constexpr (KREG > 0) {
 #pragma unroll
-      for (int j = 0; j < KREG; j++) f(base + j * 64, sv[j]);
+      for (int j = 0; j < KREG; j++) f(base + j * 64, kv[j]);
     } else {
       for (int j = 0; j < nj; j++) {
         const int i = base + j * 64;
-        f(i, load_score(i));
+        f(i, order_key(load_score(i)));
       }
     }
   }
 };
 
 // Steps 1 (after the histogram) to 3.  sm.hist holds the histogram of the
-// row under (lo, scale).  All NT threads call it together.
+// row under (lo, scale) and sm.n_cand is 0.  All NT threads call it together.
 template <int NT, int KREG, typename Load>
 __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& row, int k,
                                                       int32_t* out_idx, float* out_val,
@@ -126,7 +136,6 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
   static_assert(BPL >= 1 && kBins % (NW * 64) == 0, "bins split over the waves");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = row.S;
-  auto each = [&](auto&& f) { row.each(f); };
 
   // ---- 1b. descending scan over the bins: wave w covers positions
   // [w*kBins/NW, (w+1)*kBins/NW), position q holds bin kBins-1-q
@@ -157,31 +166,46 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
   const int rem = k - sm.sel_gt;  // 1 <= rem <= members of b*
   const int nb = sm.sel_eq;
 
-  // ---- 2. the last taken element (T, I) inside b*
+  // ---- 2. the last taken element (T, I) inside b*, and the number of taken
+  // elements of each wave's index range in sm.wcnt
   if (nb <= kFewCandidates) {
-    each([&](int i, float v) {
-      if (i < S && lin_bin(v, lo, scale) == bstar) {
-        const int slot = atomicAdd(&sm.n_cand, 1);
-        sm.cand_key[slot] = order_key(v);
-        sm.cand_idx[slot] = i;
+    // one pass: members of b* become candidates, members of higher bins are
+    // counted per wave
+    unsigned gt = 0u;
+    row.each([&](int i, unsigned key) {
+      const int bn = lin_bin(key_score(key), lo, scale);
+      const bool valid = i < S;
+      gt += (unsigned)__popcll(__ballot(valid && bn > bstar));
+      const bool cand = valid && bn == bstar;
+      if (__ballot(cand) != 0ull) {  // rare: this wave row holds members of b*
+        if (cand) {
+          const int slot = atomicAdd(&sm.n_cand, 1);
+          sm.cand_key[slot] = key;
+          sm.cand_idx[slot] = i;
+        }
       }
     });
+    if (lane == 0) sm.wcnt[wave] = (int)gt;
     __syncthreads();
     if (wave == 0) {
+      // candidate m on lane m; rank = members ordered before it by
+      // (key descending, index ascending)
       const bool mine = lane < nb;
       const unsigned mk = mine ? sm.cand_key[lane] : 0u;
       const int mi = mine ? sm.cand_idx[lane] : INT_MAX;
       int rank = 0;
       for (int m = 0; m < nb; m++) {
-        const unsigned ok = sm.cand_key[m];
-        const int oi = sm.cand_idx[m];
+        const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, m);
+        const int oi = __builtin_amdgcn_readlane(mi, m);
         rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
       }
       if (mine && rank == rem - 1) {  // exactly one lane
         sm.thr_key = mk;
         sm.thr_idx = mi;
       }
+      if (mine && rank < rem) atomicAdd(&sm.wcnt[mi / row.per_wave], 1);
     }
+    __syncthreads();
   } else {
     // radix passes over the keys of b*'s members
     unsigned prefix = 0u, pmask = 0u;
@@ -191,11 +215,9 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
       const int shift = 24 - 8 * pass;
       for (int e = tid; e < NW * 256; e += NT) (&sm.whist[0][0])[e] = 0u;
       __syncthreads();
-      each([&](int i, float v) {
-        if (i < S && lin_bin(v, lo, scale) == bstar) {
-          const unsigned key = order_key(v);
-          if ((key & pmask) == prefix) atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
-        }
+      row.each([&](int i, unsigned key) {
+        if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
+          atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
       });
       __syncthreads();
       if (wave == 0) {
@@ -234,11 +256,9 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     // passes ran); I: every key equal to T is taken if the group was taken
     // whole, else the rr-th one in index order
     unsigned tmin = 0xffffffffu;
-    each([&](int i, float v) {
-      if (i < S && lin_bin(v, lo, scale) == bstar) {
-        const unsigned key = order_key(v);
-        if ((key & pmask) == prefix) tmin = min(tmin, key);
-      }
+    row.each([&](int i, unsigned key) {
+      if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
+        tmin = min(tmin, key);
     });
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (unsigned)__shfl_xor((int)tmin, o, 64));
@@ -254,13 +274,13 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     } else {
       // the rr-th index (ascending) among keys equal to T
       int cnt = 0;
-      each([&](int i, float v) { cnt += __popcll(__ballot(i < S && order_key(v) == T)); });
+      row.each([&](int i, unsigned key) { cnt += __popcll(__ballot(i < S && key == T)); });
       if (lane == 0) sm.wcnt[wave] = cnt;
       __syncthreads();
       int seen = 0;
       for (int w = 0; w < wave; w++) seen += sm.wcnt[w];
-      each([&](int i, float v) {
-        const bool eq = i < S && order_key(v) == T;
+      row.each([&](int i, unsigned key) {
+        const bool eq = i < S && key == T;
         const unsigned long long be = __ballot(eq);
         if (eq && seen + lane_rank(be) == rr - 1) {
           sm.thr_key = T;
@@ -269,29 +289,29 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
         seen += __popcll(be);
       });
     }
+    __syncthreads();
+    const unsigned Tk = sm.thr_key;
+    const int Ik = sm.thr_idx;
+    int cnt = 0;
+    row.each([&](int i, unsigned key) {
+      cnt += __popcll(__ballot(i < S && (key > Tk || (key == Tk && i <= Ik))));
+    });
+    if (lane == 0) sm.wcnt[wave] = cnt;
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 3. ordered compaction: take key > T, or key == T with index <= I
   const unsigned T = sm.thr_key;
   const int I = sm.thr_idx;
-  auto taken = [&](int i, float v) -> bool {
-    const unsigned key = order_key(v);
-    return i < S && (key > T || (key == T && i <= I));
-  };
-  int cnt = 0;
-  each([&](int i, float v) { cnt += __popcll(__ballot(taken(i, v))); });
-  if (lane == 0) sm.wcnt[wave] = cnt;
-  __syncthreads();
   int out = 0;
   for (int w = 0; w < wave; w++) out += sm.wcnt[w];
-  each([&](int i, float v) {
-    const bool sel = taken(i, v);
+  row.each([&](int i, unsigned key) {
+    const bool sel = i < S && (key > T || (key == T && i <= I));
     const unsigned long long bs = __ballot(sel);
     const int pos = out + lane_rank(bs);
     if (sel && pos < k) {  // exactly k are taken; the bound only guards the row
       out_idx[pos] = i;
-      if (out_val) out_val[pos] = v == 0.f ? 0.f : v;  // -0 reported as +0
+      if (out_val) out_val[pos] = key_score(key);
     }
     out += __popcll(bs);
   });
@@ -310,19 +330,21 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
   select_clear<NT>(sm);
   float lo = lo_in, hi = hi_in;
   if (!have_range) {
-    lo = INFINITY;
-    hi = -INFINITY;
-    row.each([&](int i, float v) {
-      if (i < S) {
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-      }
+    // the range through the keys: integer min / max, padding excluded
+    unsigned kmin = 0xffffffffu, kmax = 0u;
+    row.each([&](int i, unsigned key) {
+      const bool valid = i < S;
+      kmin = min(kmin, valid ? key : 0xffffffffu);
+      kmax = max(kmax, valid ? key : 0u);
     });
-    lo = -wave_max(-lo);
-    hi = wave_max(hi);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, (unsigned)__shfl_xor((int)kmin, o, 64));
+      kmax = max(kmax, (unsigned)__shfl_xor((int)kmax, o, 64));
+    }
     if (lane == 0) {
-      sm.wmin[wave] = lo;
-      sm.wmax[wave] = hi;
+      sm.wmin[wave] = key_score(kmin);
+      sm.wmax[wave] = key_score(kmax);
     }
   }
   __syncthreads();
@@ -336,8 +358,8 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
     }
   }
   const float scale = bin_scale(lo, hi);
-  row.each([&](int i, float v) {
-    if (i < S) atomicAdd(&sm.hist[lin_bin(v, lo, scale)], 1u);
+  row.each([&](int i, unsigned key) {
+    if (i < S) atomicAdd(&sm.hist[lin_bin(key_score(key), lo, scale)], 1u);
   });
   __syncthreads();
   select_from_histogram<NT, KREG>(row, k, out_idx, out_val, sm, lo, scale);
