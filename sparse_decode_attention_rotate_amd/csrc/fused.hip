@@ -249,29 +249,12 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   __syncthreads();
 
   // ---- 2. top-k of each head's scores, from LDS
-  if (G == 1) {
-    auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
-    RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
-    select_from_histogram<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale);
-    __syncthreads();
-  } else {
-    for (int h = 0; h < G; h++) {
-      float l0 = rng[0][0][h], h0 = rng[1][0][h];
-#pragma unroll
-      for (int w = 1; w < NW; w++) {
-        l0 = fminf(l0, rng[0][w][h]);
-        h0 = fmaxf(h0, rng[1][w][h]);
-      }
-      const float* row = sc + h * S;
-      auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
-      block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0,
-                                   h0);
-      __syncthreads();
-    }
-  }
-
-  // ---- 0''. finish the rotation: qs[h][DP:D]
-  {
+  // Single head (k within the per-wave list capacity): the selected rows come
+  // in two index-ordered parts and the attention starts as soon as they are
+  // known; the partial rotation sums go to LDS inside the selection's barriers.
+  constexpr bool kStreamRows = G == 1;
+  const bool stream_rows = kStreamRows && k <= kBins / NW;
+  auto rotate_rest = [&]() {  // qpart[w][h][DP:D] from the P loads in flight
     float a[G][4];
 #pragma unroll
     for (int h = 0; h < G; h++)
@@ -297,26 +280,63 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
       for (int h = 0; h < G; h++)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) qpart[wave][h][DP + 4 * cqr + cc] = a[h][cc];
-  }
-  __syncthreads();
-  for (int e = tid; e < G * (D - DP); e += NT) {
-    const int h = e / (D - DP), j = DP + e % (D - DP);
-    float s = 0.f;
+  };
+  auto reduce_rest = [&]() {  // qs[h][DP:D] = sum over the waves of qpart
+    for (int e = tid; e < G * (D - DP); e += NT) {
+      const int h = e / (D - DP), j = DP + e % (D - DP);
+      float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; w++) s += qpart[w][h][j];
-    qs[h][j] = s;
+      for (int w = 0; w < NW; w++) s += qpart[w][h][j];
+      qs[h][j] = s;
+    }
+  };
+  if (stream_rows) {
+    auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
+    RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
+    select_rows<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale, rotate_rest);
+    reduce_rest();
+    __syncthreads();
+  } else {
+    if (G == 1) {
+      auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
+      RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
+      select_from_histogram<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale);
+      __syncthreads();
+    } else {
+      for (int h = 0; h < G; h++) {
+        float l0 = rng[0][0][h], h0 = rng[1][0][h];
+#pragma unroll
+        for (int w = 1; w < NW; w++) {
+          l0 = fminf(l0, rng[0][w][h]);
+          h0 = fmaxf(h0, rng[1][w][h]);
+        }
+        const float* row = sc + h * S;
+        auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
+        block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0,
+                                     h0);
+        __syncthreads();
+      }
+    }
+    // ---- 0''. finish the rotation: qs[h][DP:D]
+    rotate_rest();
+    __syncthreads();
+    reduce_rest();
+    __syncthreads();
   }
-  __syncthreads();
 
   __builtin_amdgcn_s_setprio(0);
   // ---- 3. exact attention over the selected tokens of each head
+  if (p.idx_out) {
+    if (stream_rows)
+      write_rows_in_index_order(sidx, ssm.sel_gt, k, p.idx_out + q0 * k, NT);
+    else
+      for (int e = tid; e < G * k; e += NT) p.idx_out[q0 * k + e] = sidx[e];
+  }
   for (int h = 0; h < G; h++) {
     float M, L, A;
     block_attend<DT, D, NT, true, kFusedRowsPerBatch>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
                                   p.kcache, p.vcache, head, sh, asm_, M, L, A);
     if (tid < D) p.out[(q0 + h) * D + tid] = A / L;
-    if (p.idx_out)
-      for (int r = tid; r < k; r += NT) p.idx_out[(q0 + h) * k + r] = sidx[h * k + r];
     __syncthreads();  // asm_ is reused by the next head
   }
 }

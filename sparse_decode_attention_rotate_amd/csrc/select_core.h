@@ -124,21 +124,16 @@ struct RowView {
   }
 };
 
-// Steps 1 (after the histogram) to 3.  sm.hist holds the histogram of the
-// row under (lo, scale) and sm.n_cand is 0.  All NT threads call it together.
-template <int NT, int KREG, typename Load>
-__device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& row, int k,
-                                                      int32_t* out_idx, float* out_val,
-                                                      SelectSmem<NT / 64>& sm, float lo,
-                                                      float scale) {
+// Step 1b: descending scan over the histogram; sets sm.sel_bin (the bin b*
+// holding the k-th largest score), sm.sel_gt (members of higher bins) and
+// sm.sel_eq (members of b*).  All NT threads; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void select_scan(SelectSmem<NT / 64>& sm, int k) {
   constexpr int NW = NT / 64;
   constexpr int BPL = kBins / NW / 64;  // bins per lane in the scan
   static_assert(BPL >= 1 && kBins % (NW * 64) == 0, "bins split over the waves");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = row.S;
-
-  // ---- 1b. descending scan over the bins: wave w covers positions
-  // [w*kBins/NW, (w+1)*kBins/NW), position q holds bin kBins-1-q
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave w covers positions [w*kBins/NW, (w+1)*kBins/NW), position q holds bin kBins-1-q
   unsigned c[BPL];
   unsigned tot = 0u;
 #pragma unroll
@@ -162,6 +157,114 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     before = after;
   }
   __syncthreads();
+}
+
+// Step 2 for a crowded b*: radix passes over 8-bit digits of the keys of
+// b*'s members (per-wave LDS histograms) give (T, I), the last taken element,
+// in sm.thr_key / sm.thr_idx.  All NT threads; ends with a barrier.
+template <int NT, int KREG, typename Load>
+__device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, int bstar, int rem,
+                                                float lo, float scale, SelectSmem<NT / 64>& sm) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = row.S;
+  // radix passes over the keys of b*'s members
+  unsigned prefix = 0u, pmask = 0u;
+  int rr = rem;
+  bool whole = false;
+  for (int pass = 0; pass < 4; pass++) {
+    const int shift = 24 - 8 * pass;
+    for (int e = tid; e < NW * 256; e += NT) (&sm.whist[0][0])[e] = 0u;
+    __syncthreads();
+    row.each([&](int i, unsigned key) {
+      if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
+        atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
+    });
+    __syncthreads();
+    if (wave == 0) {
+      unsigned cc[4];
+      unsigned t4 = 0u;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int dg = 255 - (lane * 4 + u);
+        unsigned s = 0u;
+#pragma unroll
+        for (int w = 0; w < NW; w++) s += sm.whist[w][dg];
+        cc[u] = s;
+        t4 += s;
+      }
+      unsigned bf = wave_incl_scan(t4) - t4;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const unsigned af = bf + cc[u];
+        if (bf < (unsigned)rr && af >= (unsigned)rr) {
+          sm.r_digit = 255u - (unsigned)(lane * 4 + u);
+          sm.r_gt = bf;
+          sm.r_eq = cc[u];
+        }
+        bf = af;
+      }
+    }
+    __syncthreads();
+    rr -= (int)sm.r_gt;
+    prefix |= sm.r_digit << shift;
+    pmask |= 0xffu << shift;
+    whole = (int)sm.r_eq == rr;  // the whole prefix group is taken
+    __syncthreads();
+    if (whole) break;
+  }
+  // T: the smallest key of the taken prefix group (the exact key when all
+  // passes ran); I: every key equal to T is taken if the group was taken
+  // whole, else the rr-th one in index order
+  unsigned tmin = 0xffffffffu;
+  row.each([&](int i, unsigned key) {
+    if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
+      tmin = min(tmin, key);
+  });
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (unsigned)__shfl_xor((int)tmin, o, 64));
+  if (lane == 0) sm.wtot[wave] = tmin;
+  __syncthreads();
+  unsigned T = sm.wtot[0];
+  for (int w = 1; w < NW; w++) T = min(T, sm.wtot[w]);
+  if (whole) {
+    if (tid == 0) {
+      sm.thr_key = T;
+      sm.thr_idx = INT_MAX;
+    }
+  } else {
+    // the rr-th index (ascending) among keys equal to T
+    int cnt = 0;
+    row.each([&](int i, unsigned key) { cnt += __popcll(__ballot(i < S && key == T)); });
+    if (lane == 0) sm.wcnt[wave] = cnt;
+    __syncthreads();
+    int seen = 0;
+    for (int w = 0; w < wave; w++) seen += sm.wcnt[w];
+    row.each([&](int i, unsigned key) {
+      const bool eq = i < S && key == T;
+      const unsigned long long be = __ballot(eq);
+      if (eq && seen + lane_rank(be) == rr - 1) {
+        sm.thr_key = T;
+        sm.thr_idx = i;
+      }
+      seen += __popcll(be);
+    });
+  }
+  __syncthreads();
+}
+
+// Steps 1 (after the histogram) to 3.  sm.hist holds the histogram of the
+// row under (lo, scale) and sm.n_cand is 0.  All NT threads call it together.
+template <int NT, int KREG, typename Load>
+__device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& row, int k,
+                                                      int32_t* out_idx, float* out_val,
+                                                      SelectSmem<NT / 64>& sm, float lo,
+                                                      float scale) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = row.S;
+
+  select_scan<NT>(sm, k);
   const int bstar = sm.sel_bin;
   const int rem = k - sm.sel_gt;  // 1 <= rem <= members of b*
   const int nb = sm.sel_eq;
@@ -207,89 +310,7 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     __syncthreads();
   } else {
-    // radix passes over the keys of b*'s members
-    unsigned prefix = 0u, pmask = 0u;
-    int rr = rem;
-    bool whole = false;
-    for (int pass = 0; pass < 4; pass++) {
-      const int shift = 24 - 8 * pass;
-      for (int e = tid; e < NW * 256; e += NT) (&sm.whist[0][0])[e] = 0u;
-      __syncthreads();
-      row.each([&](int i, unsigned key) {
-        if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
-          atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
-      });
-      __syncthreads();
-      if (wave == 0) {
-        unsigned cc[4];
-        unsigned t4 = 0u;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const int dg = 255 - (lane * 4 + u);
-          unsigned s = 0u;
-#pragma unroll
-          for (int w = 0; w < NW; w++) s += sm.whist[w][dg];
-          cc[u] = s;
-          t4 += s;
-        }
-        unsigned bf = wave_incl_scan(t4) - t4;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const unsigned af = bf + cc[u];
-          if (bf < (unsigned)rr && af >= (unsigned)rr) {
-            sm.r_digit = 255u - (unsigned)(lane * 4 + u);
-            sm.r_gt = bf;
-            sm.r_eq = cc[u];
-          }
-          bf = af;
-        }
-      }
-      __syncthreads();
-      rr -= (int)sm.r_gt;
-      prefix |= sm.r_digit << shift;
-      pmask |= 0xffu << shift;
-      whole = (int)sm.r_eq == rr;  // the whole prefix group is taken
-      __syncthreads();
-      if (whole) break;
-    }
-    // T: the smallest key of the taken prefix group (the exact key when all
-    // passes ran); I: every key equal to T is taken if the group was taken
-    // whole, else the rr-th one in index order
-    unsigned tmin = 0xffffffffu;
-    row.each([&](int i, unsigned key) {
-      if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
-        tmin = min(tmin, key);
-    });
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (unsigned)__shfl_xor((int)tmin, o, 64));
-    if (lane == 0) sm.wtot[wave] = tmin;
-    __syncthreads();
-    unsigned T = sm.wtot[0];
-    for (int w = 1; w < NW; w++) T = min(T, sm.wtot[w]);
-    if (whole) {
-      if (tid == 0) {
-        sm.thr_key = T;
-        sm.thr_idx = INT_MAX;
-      }
-    } else {
-      // the rr-th index (ascending) among keys equal to T
-      int cnt = 0;
-      row.each([&](int i, unsigned key) { cnt += __popcll(__ballot(i < S && key == T)); });
-      if (lane == 0) sm.wcnt[wave] = cnt;
-      __syncthreads();
-      int seen = 0;
-      for (int w = 0; w < wave; w++) seen += sm.wcnt[w];
-      row.each([&](int i, unsigned key) {
-        const bool eq = i < S && key == T;
-        const unsigned long long be = __ballot(eq);
-        if (eq && seen + lane_rank(be) == rr - 1) {
-          sm.thr_key = T;
-          sm.thr_idx = i;
-        }
-        seen += __popcll(be);
-      });
-    }
-    __syncthreads();
+    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm);
     const unsigned Tk = sm.thr_key;
     const int Ik = sm.thr_idx;
     int cnt = 0;
@@ -315,6 +336,136 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     out += __popcll(bs);
   });
+}
+
+// Selection for a caller that attends over the selected rows right away.
+// Rows [0, sel_gt) are the members of the bins above b*, in index order: one
+// pass appends them to per-wave lists kept in sm.hist (the scan no longer
+// needs it) while it collects b*'s members; rows [sel_gt, k) are the taken
+// members of b*, also in index order.  mid() runs between that pass and the
+// barrier after it.  Writes rows_idx / rows_val (score, -0 as +0) [0, k) and
+// sm.sel_gt; the caller needs a barrier before reading them.
+// Requires k <= kBins / (NT / 64) (the lists' capacity).
+template <int NT, int KREG, typename Load, typename Mid>
+__device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k, int32_t* rows_idx,
+                                            float* rows_val, SelectSmem<NT / 64>& sm, float lo,
+                                            float scale, Mid&& mid) {
+  constexpr int NW = NT / 64;
+  constexpr int CAP = kBins / NW;  // > sel_gt >= the length of any wave's list
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = row.S;
+
+  select_scan<NT>(sm, k);
+  const int bstar = sm.sel_bin, sel_gt = sm.sel_gt, rem = k - sel_gt, nb = sm.sel_eq;
+  const bool few = nb <= kFewCandidates;
+  int* lists = reinterpret_cast<int*>(sm.hist);
+
+  int cnt = 0;
+  row.each([&](int i, unsigned key) {
+    const int bn = lin_bin(key_score(key), lo, scale);
+    const bool valid = i < S;
+    const bool sure = valid && bn > bstar;
+    const unsigned long long bs = __ballot(sure);
+    if (sure) lists[wave * CAP + cnt + lane_rank(bs)] = i;
+    cnt += __popcll(bs);
+    const bool cand = few && valid && bn == bstar;
+    if (__ballot(cand) != 0ull) {  // rare: this wave row holds members of b*
+      if (cand) {
+        const int slot = atomicAdd(&sm.n_cand, 1);
+        sm.cand_key[slot] = key;
+        sm.cand_idx[slot] = i;
+      }
+    }
+  });
+  if (lane == 0) sm.wcnt[wave] = cnt;
+  mid();
+  __syncthreads();
+
+  // rows [0, sel_gt): the per-wave lists back to back
+  int pre[NW];
+  pre[0] = 0;
+#pragma unroll
+  for (int w = 1; w < NW; w++) pre[w] = pre[w - 1] + sm.wcnt[w - 1];
+  for (int r = tid; r < sel_gt; r += NT) {
+    int w = 0;
+#pragma unroll
+    for (int v = 1; v < NW; v++) w += r >= pre[v] ? 1 : 0;
+    const int i = lists[w * CAP + r - pre[w]];
+    rows_idx[r] = i;
+    rows_val[r] = key_score(order_key(row.load_score(i)));
+  }
+
+  // rows [sel_gt, k): the taken members of b*
+  if (few) {
+    if (wave == 0) {
+      // candidate m on lane m; rank = members ordered before it by
+      // (key descending, index ascending); the rem first are taken
+      const bool mine = lane < nb;
+      const unsigned mk = mine ? sm.cand_key[lane] : 0u;
+      const int mi = mine ? sm.cand_idx[lane] : INT_MAX;
+      int rank = 0;
+      for (int m = 0; m < nb; m++) {
+        const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, m);
+        const int oi = __builtin_amdgcn_readlane(mi, m);
+        rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+      }
+      const bool taken = mine && rank < rem;
+      int pos = 0;  // among the taken, by index
+      for (int m = 0; m < nb; m++) {
+        const int orank = __builtin_amdgcn_readlane(rank, m);
+        const int oi = __builtin_amdgcn_readlane(mi, m);
+        pos += (orank < rem && oi < mi) ? 1 : 0;
+      }
+      if (taken) {
+        rows_idx[sel_gt + pos] = mi;
+        rows_val[sel_gt + pos] = key_score(mk);
+      }
+    }
+  } else {
+    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm);
+    const unsigned T = sm.thr_key;
+    const int I = sm.thr_idx;
+    auto taken = [&](int i, unsigned key) -> bool {
+      return i < S && lin_bin(key_score(key), lo, scale) == bstar &&
+             (key > T || (key == T && i <= I));
+    };
+    int c2 = 0;
+    row.each([&](int i, unsigned key) { c2 += __popcll(__ballot(taken(i, key))); });
+    if (lane == 0) sm.wcnt[wave] = c2;
+    __syncthreads();
+    int out = sel_gt;
+    for (int w = 0; w < wave; w++) out += sm.wcnt[w];
+    row.each([&](int i, unsigned key) {
+      const bool t = taken(i, key);
+      const unsigned long long bt = __ballot(t);
+      const int pos = out + lane_rank(bt);
+      if (t && pos < k) {
+        rows_idx[pos] = i;
+        rows_val[pos] = key_score(key);
+      }
+      out += __popcll(bt);
+    });
+  }
+}
+
+// The rows of select_rows in ascending index order, to global memory: the two
+// index-ordered parts [0, n1) and [n1, k) merged by binary search (all NT
+// threads, after the rows are visible).
+__device__ __forceinline__ void write_rows_in_index_order(const int32_t* rows, int n1, int k,
+                                                          int32_t* out, int NT) {
+  auto lower = [&](int from, int n, int t) {  // first position in rows[from, from+n) >= t
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (rows[from + mid] < t) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  for (int r = threadIdx.x; r < k; r += NT) {
+    const int t = rows[r];
+    const int pos = r < n1 ? r + lower(n1, k - n1, t) : (r - n1) + lower(0, n1, t);
+    out[pos] = t;
+  }
 }
 
 // Whole selection from the scores alone (range, histogram, steps 1-3).
