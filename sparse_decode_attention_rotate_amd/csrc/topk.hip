@@ -35,6 +35,8 @@ hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st) {
     topk_kernel<512, 8><<<grid, 512, 0, st>>>(p);
   else if (p.S <= 1024 * 16)
     topk_kernel<1024, 16><<<grid, 1024, 0, st>>>(p);
+  else if (p.S <= 1024 * 32)
+    topk_kernel<1024, 32><<<grid, 1024, 0, st>>>(p);
   else
     topk_kernel<1024, 0><<<grid, 1024, 0, st>>>(p);
   return hipGetLastError();

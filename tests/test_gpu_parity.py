@@ -265,6 +265,7 @@ E2E = {
     "cap-above-seq": dict(dtype="f16", S=1900, S_cap=2600, k=200),
     "d64-head": dict(dtype="f16", D=64, d=16, tau=20.0),
     "long-11k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=11000, k=1375),
+    "long-30k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=30000, k=3000, heavy_frac=0.02),
     "long-40k": dict(dtype="f16", B=1, Hq=1, Hkv=1, S=40000, k=5000),
 }
 
