@@ -29,8 +29,9 @@ namespace loki {
 
 namespace {
 
-constexpr int kFusedThreads = 256;
-constexpr int kFusedKreg = 16;            // S <= 256 * 16
+// 256 threads when the units fill the GPU several times over, 512 when there
+// are no more units than compute units (more loads in flight per unit).
+constexpr int kFusedMaxS = 4096;          // scores of a unit held in registers for select
 constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per batch
 constexpr size_t kFusedDynBytes = 36 * 1024;
 #ifndef LOKI_FUSED_RB
@@ -38,10 +39,10 @@ constexpr size_t kFusedDynBytes = 36 * 1024;
 #endif
 constexpr int kFusedRowsPerBatch = LOKI_FUSED_RB;  // gather rows per lane group per batch
 
-template <int DT, int D, int LPT, int G>
-__global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) {
-  constexpr int NT = kFusedThreads;
+template <int DT, int D, int LPT, int G, int NT>
+__global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParams p) {
   constexpr int NW = NT / 64;
+  constexpr int KREG = kFusedMaxS / NT;  // order keys per thread in the selection
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int DP = LPT * 16 / Elem<DT>::kBytes;  // panel width (== d)
   constexpr int TPP = NT / LPT;                    // tokens per pass over the panel
@@ -292,15 +293,15 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   };
   if (stream_rows) {
     auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
-    RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
-    select_rows<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale, rotate_rest);
+    RowView<NT, KREG, decltype(load_score)> row(load_score, S);
+    select_rows<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, rotate_rest);
     reduce_rest();
     __syncthreads();
   } else {
     if (G == 1) {
       auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
-      RowView<NT, kFusedKreg, decltype(load_score)> row(load_score, S);
-      select_from_histogram<NT, kFusedKreg>(row, k, sidx, slow, ssm, blo, bscale);
+      RowView<NT, KREG, decltype(load_score)> row(load_score, S);
+      select_from_histogram<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale);
       __syncthreads();
     } else {
       for (int h = 0; h < G; h++) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
         }
         const float* row = sc + h * S;
         auto load_score = [&](int i) -> float { return i < S ? row[i] : 0.f; };
-        block_select<NT, kFusedKreg>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0,
+        block_select<NT, KREG>(load_score, S, k, sidx + h * k, slow + h * k, ssm, true, l0,
                                      h0);
         __syncthreads();
       }
@@ -341,15 +342,21 @@ __global__ __launch_bounds__(kFusedThreads, 3) void fused_kernel(FusedParams p) 
   }
 }
 
-template <int DT, int D, int LPT>
-hipError_t launch_lpt(const FusedParams& p, size_t dyn, hipStream_t st) {
+template <int DT, int D, int LPT, int NT>
+hipError_t launch_nt(const FusedParams& p, size_t dyn, hipStream_t st) {
   const dim3 grid((unsigned)(p.sh.B * p.sh.Hkv));
   switch (p.sh.g) {
-    case 1: fused_kernel<DT, D, LPT, 1><<<grid, kFusedThreads, dyn, st>>>(p); break;
-    case 2: fused_kernel<DT, D, LPT, 2><<<grid, kFusedThreads, dyn, st>>>(p); break;
-    default: fused_kernel<DT, D, LPT, 4><<<grid, kFusedThreads, dyn, st>>>(p); break;
+    case 1: fused_kernel<DT, D, LPT, 1, NT><<<grid, NT, dyn, st>>>(p); break;
+    case 2: fused_kernel<DT, D, LPT, 2, NT><<<grid, NT, dyn, st>>>(p); break;
+    default: fused_kernel<DT, D, LPT, 4, NT><<<grid, NT, dyn, st>>>(p); break;
   }
   return hipGetLastError();
+}
+
+template <int DT, int D, int LPT>
+hipError_t launch_lpt(const FusedParams& p, size_t dyn, hipStream_t st) {
+  return p.threads == 512 ? launch_nt<DT, D, LPT, 512>(p, dyn, st)
+                          : launch_nt<DT, D, LPT, 256>(p, dyn, st);
 }
 
 template <int DT>
@@ -368,7 +375,7 @@ bool fused_supported(const Shape& sh, int d, int k) {
   const int eb = sh.dtype == F32 ? 4 : 2;
   const int lpt = sh.dp * eb / 16;
   return d == sh.dp && sh.D == 128 && (lpt == 4 || lpt == 8) &&
-         (sh.g == 1 || sh.g == 2 || sh.g == 4) && sh.S <= kFusedThreads * kFusedKreg &&
+         (sh.g == 1 || sh.g == 2 || sh.g == 4) && sh.S <= kFusedMaxS &&
          dyn_bytes(sh, k) <= kFusedDynBytes;
 }
 

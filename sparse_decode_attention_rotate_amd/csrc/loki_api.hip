@@ -108,6 +108,20 @@ WsLayout ws_layout(const Shape& sh, int k) {
   return w;
 }
 
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 float scale_log2(const loki_desc* d) {
   const float s = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
   return s * 1.4426950408889634f;  // log2(e)
@@ -156,6 +170,9 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     fp.k = k;
     fp.scale_log2 = scale_log2(desc);
     fp.sh = sh;
+    // one workgroup per (b, kv): with no more of them than compute units, use
+    // 512 threads so that each unit has twice the loads in flight
+    fp.threads = (long)sh.B * sh.Hkv <= compute_units() ? 512 : 256;
     return hip_status(launch_fused(fp, st), "fused");
   }
 

@@ -66,6 +66,7 @@ struct FusedParams {
   int32_t* idx_out;     // [B,Hq,k] nullable
   int k;
   float scale_log2;
+  int threads;          // workgroup size: 256 or 512
   Shape sh;
 };
 
