@@ -174,6 +174,37 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       for (int e = 0; e < E; e++) qv[h][e] = qs[h][c * E + e];  // c*E < DP == d
     }
     auto consume = [&](const u32x4 (&x)[NB], int pass0, bool hist) {
+      if constexpr (G == 1 && LPT == 4 && NB % 4 == 0) {
+        // Each lane's partial dot product for each pass of the batch, then a
+        // reduce-scatter over groups of 4 passes: lane c of a quad ends with
+        // the whole score of pass (group + c) and stores and bins it itself.
+        // The pairs are added as in group_sum<4>, so the scores are the same.
+        float a[NB];
+#pragma unroll
+        for (int it = 0; it < NB; it++) {
+          float f[E];
+          unpack16<DT>(x[it], f);
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; e++) acc = fmaf(qv[0][e], f[e], acc);
+          a[it] = acc;
+        }
+        const bool b0 = (c & 1) != 0, b1 = (c & 2) != 0;
+#pragma unroll
+        for (int g0 = 0; g0 < NB; g0 += 4) {
+          const float u0 = (b0 ? a[g0 + 1] : a[g0]) + dpp_f<0xB1>(b0 ? a[g0] : a[g0 + 1]);
+          const float u1 = (b0 ? a[g0 + 3] : a[g0 + 2]) + dpp_f<0xB1>(b0 ? a[g0 + 2] : a[g0 + 3]);
+          const float r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
+          const int t = (pass0 + g0 + c) * TPP + tl;
+          if (t < S) {
+            lo[0] = fminf(lo[0], r);
+            hi[0] = fmaxf(hi[0], r);
+            sc[t] = r;
+            if (hist) atomicAdd(&ssm.hist[lin_bin(r, blo, bscale)], 1u);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int it = 0; it < NB; it++) {
         float f[E];
