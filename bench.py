@@ -210,6 +210,17 @@ def main():
     }
     per_kernel = {n: round(u, 2) for n, u in per_kernel.items()}
 
+    # dense decode attention over all S tokens on the same caches: the baseline
+    # the pages measure Loki's attention speed-up against
+    ws_full = loki.empty_workspace(desc, wl.D, wl.S)
+    wsf_ = vp(ws_full.data_ptr())
+    chk(lib.loki_full_attention(q_, kcs[0], vcs[0], P_, out_, cd, wsf_, ws_full.numel(), st))
+    full_us = timed(lambda i: lib.loki_full_attention(q_, kcs[i % len(kcs)], vcs[i % len(vcs)], P_,
+                                                      out_, cd, wsf_, ws_full.numel(), st))
+    es_ = 4 if wl.dtype == "f32" else 2
+    full_bytes = es_ * wl.B * wl.Hkv * wl.S * wl.D * 2
+    del ws_full
+
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()
     score_bytes = es * wl.B * wl.Hkv * wl.S * wl.d
@@ -247,6 +258,9 @@ def main():
         "launch_plan": "one kernel" if one_launch else "separate kernels",
         "kernel_us": kernels,
         "separate_launches": {"us_per_step": round(sep_step_us, 2), "kernel_us": per_kernel},
+        "full_attention": {"us_per_step": round(full_us, 2), "kv_bytes_per_step": full_bytes,
+                           "GBps": round(full_bytes / (full_us * 1e-6) / 1e9, 1),
+                           "loki_speedup": round(full_us / (ms_per_step * 1e3), 3)},
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

@@ -186,6 +186,20 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
                        int32_t* idx_out, const loki_desc* desc, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * Dense decode attention over all S cached tokens, the baseline the pages
+ * measure Loki against ([T] "TL;DR" and [S]: speed-up of Loki's attention
+ * over vanilla attention): qr = q . P[kv], z_t = scale * qr . krot_t over all
+ * D coordinates of every token t < S, out = softmax(z) . V.  Because P is
+ * orthonormal, qr . krot_t = q . k_t: this is ordinary full attention, read
+ * from the same rotated cache.  out [B, Hq, D] fp32.  Split over chunks of
+ * the sequence; partial softmax states are merged by a second launch.
+ * Needs loki_workspace_bytes(desc, D, seq_len) bytes of workspace.
+ */
+int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
+                        float* out, const loki_desc* desc, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ STATUS = {0: "LOKI_OK", -1: "LOKI_EINVAL", -2: "LOKI_EUNSUPPORTED", -3: "LOKI_EW
 EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_workspace_bytes",
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
-           "loki_decode_plan"]
+           "loki_decode_plan", "loki_full_attention"]
 
 
 class _CDesc(ctypes.Structure):
@@ -67,6 +67,7 @@ _SIG = {
     "loki_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _D, _vp, _sz, _vp],
                            _i),
     "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
+    "loki_full_attention": ([_vp, _vp, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(_lib, _name)
@@ -274,6 +275,21 @@ def decode_append(q, k_new, v_new, kcache, vcache, P, d: int, k: int, desc: Desc
                                    _ptr(P), d, k, _ptr(out), _ptr(idx_out), ctypes.byref(desc.c()),
                                    _ptr(workspace), workspace.numel(), _stream(stream)),
            "loki_decode_append")
+    return out
+
+
+def full_attention(q, kcache, vcache, P, desc: Desc, out=None, workspace=None, stream=None):
+    """Dense decode attention over all seq_len cached tokens (the baseline of
+    the Loki step); returns out [B, Hq, D] fp32."""
+    _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    if workspace is None:
+        workspace = empty_workspace(desc, desc.head_dim, desc.seq_len, q.device)
+    _check(_lib.loki_full_attention(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), _ptr(out),
+                                    ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "loki_full_attention")
     return out
 
 

@@ -8,6 +8,10 @@
 // indices in LDS and runs block_attend (attend_core.h) over them.  With one
 // split it writes the output row; otherwise it writes (m, l, acc[D]) in the
 // log2 domain and combine_kernel merges the splits.
+//
+// Without an index list (idx == null) row r is token r: dense decode
+// attention over all S cached tokens, the full-attention baseline the pages
+// compare Loki with (poster page "TL;DR": speed-up over vanilla attention).
 #include "attend_core.h"
 #include "loki_internal.h"
 
@@ -34,7 +38,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
 
   // the chunk's token indices (invalid ones as -1) and low-dim partial logits
   for (int r = tid; r < nr; r += kAttThreads) {
-    const int t = p.idx[bh * p.k + r0 + r];
+    const int t = p.idx ? p.idx[bh * p.k + r0 + r] : r0 + r;
     sidx[r] = (t >= 0 && t < sh.S) ? t : -1;
     if (SPLIT) slow[r] = p.sel_scores[bh * p.k + r0 + r];
   }

@@ -422,4 +422,49 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
                      workspace_bytes, stream, true);
 }
 
+int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
+                        float* out, const loki_desc* desc, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kcache);
+  REQUIRE_PTR(vcache);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(workspace);
+  const WsLayout w = ws_layout(sh, sh.S);
+  if (workspace_bytes < w.total)
+    return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  float* qr = reinterpret_cast<float*>(ws + w.qr);
+
+  ProjectParams pp{};
+  pp.q = q;
+  pp.P = P;
+  pp.qr = qr;
+  pp.kcache = const_cast<void*>(kcache);
+  pp.vcache = const_cast<void*>(vcache);
+  pp.sh = sh;
+  if ((rc = hip_status(launch_project(pp, st), "project"))) return rc;
+
+  AttendParams ap{};
+  ap.qr = qr;
+  ap.kcache = kcache;
+  ap.vcache = vcache;
+  ap.idx = nullptr;  // every cached token
+  ap.sel_scores = nullptr;
+  ap.out = out;
+  ap.part = reinterpret_cast<float*>(ws + w.part);
+  ap.k = sh.S;
+  ap.d = sh.D;
+  ap.nsplit = w.nsplit;
+  ap.kc = kAttendChunk;
+  ap.scale_log2 = scale_log2(desc);
+  ap.sh = sh;
+  return hip_status(launch_attend(ap, st), "attend");
+}
+
 }  // extern "C"

@@ -48,7 +48,7 @@ struct AttendParams {
   const float* qr;          // [B,Hq,D]
   const void* kcache;
   const void* vcache;
-  const int32_t* idx;       // [B*Hq, k]
+  const int32_t* idx;       // [B*Hq, k]; null: row r is token r (k = S, dense attention)
   const float* sel_scores;  // [B*Hq, k] low-dim partial logits (split variant) or null
   float* out;               // [B,Hq,D] fp32 (written when nsplit == 1 or by combine)
   float* part;              // [B*Hq, nsplit, D+2] partial (m, l, acc)

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["loki_decode", "loki_decode_append", "loki_append", "loki_rotate_query",
               "loki_score", "loki_topk", "loki_attend", "loki_pack_kcache", "loki_unpack_kcache",
-              "loki_workspace_bytes", "loki_kcache_elems", "loki_strerror", "loki_last_error"]:
+              "loki_workspace_bytes", "loki_kcache_elems", "loki_strerror", "loki_last_error",
+              "loki_decode_plan", "loki_full_attention"]:
         assert n in names
 
 
@@ -108,6 +109,7 @@ def test_other_entry_points_validate(L):
     d = _desc(L)
     cd = ctypes.byref(d.c())
     fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
     lib = L.lib
     assert lib.loki_append(fake, fake, fake, fake, fake, 128, cd, None) == -1   # pos >= S_cap
     assert lib.loki_append(fake, fake, fake, fake, fake, -1, cd, None) == -1
@@ -122,6 +124,11 @@ def test_other_entry_points_validate(L):
     assert lib.loki_unpack_kcache(fake, -1, fake, cd, None) == -1
     assert lib.loki_decode_append(fake, None, fake, fake, fake, fake, 32, 10, fake, None, cd,
                                   fake, 1 << 30, None) == -1
+    fa = lib.loki_full_attention
+    assert fa(fake, fake, fake, fake, None, cd, fake, 1 << 30, None) == -1  # out NULL
+    assert fa(odd, fake, fake, fake, fake, cd, fake, 1 << 30, None) == -1   # misaligned q
+    assert fa(fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == -1  # desc NULL
+    assert fa(fake, fake, fake, fake, fake, cd, fake, 16, None) == -3       # workspace
 
 
 def test_binding_has_no_cpu_path(L):

@@ -340,6 +340,24 @@ def test_repeat_runs_are_bit_identical(L):
         assert np.array_equal(o1, o2) and np.array_equal(i1, i2)
 
 
+# ------------------------------------------------ dense decode attention
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,S", [("f16", 4, 4, 3000), ("bf16", 8, 2, 1111),
+                                           ("f32", 2, 2, 700), ("f16", 4, 4, 1)])
+def test_full_attention(L, dtype, Hq, Hkv, S):
+    """Dense attention over every cached token: the oracle's decode with
+    d = D, k = S (pinned to textbook softmax(q K^T / sqrt(D)) V)."""
+    wl = _small(dtype, Hq=Hq, Hkv=Hkv, S=S, k=min(S, 300), d=min(S, 32))
+    H.log(f"full attention {dtype} Hq={Hq} Hkv={Hkv} S={S}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    out = L.full_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], dev["desc"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    ref = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.D, S, dtype)["out"]
+    assert H.rel_err_rows(out, ref).max() < H.OUT_TOL[dtype]
+
+
 # ---------------------------------------------------- the five workloads
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
