@@ -34,6 +34,7 @@ struct ScoreParams {
   float* scores;       // [B,Hq,S]
   int d;
   int n_tiles;         // tiles per (b, kv)
+  int tile_tokens;     // tokens per tile (panel kernel)
   Shape sh;
 };
 

@@ -131,12 +131,10 @@ hipError_t launch_project(const ProjectParams& p0, hipStream_t st) {
   ProjectParams p = p0;
   const int per_b = (p.q ? p.sh.g : 0) + (p.k_new ? 1 : 0);
   if (per_b == 0) return hipSuccess;
-  // a few batch rows per workgroup: P is re-read from L2 by each workgroup,
-  // and more workgroups shorten the latency of this small step
-  p.bb = kMaxRows / per_b;
-  if (p.bb > 4) p.bb = 4;
-  if (p.bb > p.sh.B) p.bb = p.sh.B;
-  if (p.bb < 1) return hipErrorInvalidValue;  // g too large for one workgroup
+  // one batch row per workgroup: P is re-read from L2 by each workgroup, and
+  // more workgroups shorten the latency of this small step
+  p.bb = 1;
+  if (per_b > kMaxRows) return hipErrorInvalidValue;  // g too large for one workgroup
   dim3 grid(p.sh.Hkv, (p.sh.B + p.bb - 1) / p.bb);
   p.stream = st;
   const int rows = p.bb * per_b;

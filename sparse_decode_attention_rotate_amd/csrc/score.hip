@@ -17,13 +17,14 @@ namespace loki {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreIters = 16;  // 16-byte loads in flight per lane
+constexpr int kScoreBatch = 8;  // 16-byte loads per lane per batch; two batches in flight
 
+// One workgroup streams a tile of p.tile_tokens tokens of one (b, kv) panel.
 template <int DT, int LPT, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams p) {
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int TPP = kScoreThreads / LPT;  // tokens per pass
-  constexpr int TILE = TPP * kScoreIters;
+  constexpr int NB = kScoreBatch;
   const Shape& sh = p.sh;
 
   const int tile = blockIdx.x % p.n_tiles;
@@ -31,20 +32,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
   const int c = threadIdx.x % LPT;
   const int tl = threadIdx.x / LPT;
-  const int t0 = tile * TILE;
+  const int t0 = tile * p.tile_tokens;
+  const int t_end = min(sh.S, t0 + p.tile_tokens);
+  const int n_pass = (t_end - t0 + TPP - 1) / TPP;
 
-  // the panel of this (b, kv): S_cap rows of LPT*16 bytes; tokens >= S read as zeros
+  // the panel of this (b, kv): S_cap rows of LPT*16 bytes; tokens past the
+  // tile read as zeros
   const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
                                  head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
                              (uint32_t)((size_t)sh.S_cap * LPT * 16));
-  u32x4 x[kScoreIters];
+  auto issue = [&](u32x4 (&x)[NB], int pass0) {
 #pragma unroll
-  for (int it = 0; it < kScoreIters; it++) {
-    const int t = t0 + it * TPP + tl;
-    x[it] = load16(prs, t < sh.S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
-  }
+    for (int it = 0; it < NB; it++) {
+      const int t = t0 + (pass0 + it) * TPP + tl;
+      x[it] = load16(prs, t < t_end ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+    }
+  };
+  u32x4 xa[NB], xb[NB];
+  issue(xa, 0);
+  issue(xb, NB);
 
-  // qr slices (issued after the panel loads so both are in flight)
+  // qr slices (issued after the first panel loads so both are in flight)
   float qv[G][E];
 #pragma unroll
   for (int h = 0; h < G; h++) {
@@ -58,24 +66,56 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   }
 
   float* srow = p.scores + ((size_t)b * sh.Hq + (size_t)kv * G) * sh.S;
+  auto consume = [&](const u32x4 (&x)[NB], int pass0) {
+    if constexpr (G == 1 && LPT == 4 && NB % 4 == 0) {
+      // reduce-scatter over groups of 4 passes: lane c of a quad ends with the
+      // whole score of pass (group + c) (pairs added as in group_sum<4>)
+      float a[NB];
 #pragma unroll
-  for (int it = 0; it < kScoreIters; it++) {
-    float f[E];
-    unpack16<DT>(x[it], f);
-    float s[G];
+      for (int it = 0; it < NB; it++) {
+        float f[E];
+        unpack16<DT>(x[it], f);
+        float acc = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-      float a = 0.f;
+        for (int e = 0; e < E; e++) acc = fmaf(qv[0][e], f[e], acc);
+        a[it] = acc;
+      }
+      const bool b0 = (c & 1) != 0, b1 = (c & 2) != 0;
 #pragma unroll
-      for (int e = 0; e < E; e++) a = fmaf(qv[h][e], f[e], a);
-      s[h] = group_sum<LPT>(a);
+      for (int g0 = 0; g0 < NB; g0 += 4) {
+        const float u0 = (b0 ? a[g0 + 1] : a[g0]) + dpp_f<0xB1>(b0 ? a[g0] : a[g0 + 1]);
+        const float u1 = (b0 ? a[g0 + 3] : a[g0 + 2]) + dpp_f<0xB1>(b0 ? a[g0 + 2] : a[g0 + 3]);
+        const float r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
+        const int t = t0 + (pass0 + g0 + c) * TPP + tl;
+        if (t < t_end) srow[t] = r;
+      }
+      return;
     }
-    const int t = t0 + it * TPP + tl;
-    if (t < sh.S) {
 #pragma unroll
-      for (int h = 0; h < G; h++)
-        if (c == (h % LPT)) srow[(size_t)h * sh.S + t] = s[h];
+    for (int it = 0; it < NB; it++) {
+      float f[E];
+      unpack16<DT>(x[it], f);
+      float s[G];
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) a = fmaf(qv[h][e], f[e], a);
+        s[h] = group_sum<LPT>(a);
+      }
+      const int t = t0 + (pass0 + it) * TPP + tl;
+      if (t < t_end) {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+          if (c == (h % LPT)) srow[(size_t)h * sh.S + t] = s[h];
+      }
     }
+  };
+  for (int pass = 0; pass < n_pass; pass += 2 * NB) {
+    consume(xa, pass);
+    if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
+    consume(xb, pass + NB);
+    if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
   }
 }
 
@@ -100,8 +140,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
 
 template <int DT, int LPT>
 hipError_t launch_lpt(ScoreParams p, hipStream_t st) {
-  constexpr int TILE = (kScoreThreads / LPT) * kScoreIters;
-  p.n_tiles = (p.sh.S + TILE - 1) / TILE;
+  // tiles of up to 4096 tokens (256 KB of an fp16 panel), smaller when that
+  // leaves fewer than two workgroups per compute unit; multiples of two batches
+  constexpr int STEP = (kScoreThreads / LPT) * 2 * kScoreBatch;
+  const long long units = (long long)p.sh.B * p.sh.Hkv;
+  long long want = (long long)p.sh.S * units / 512;
+  want = want < STEP ? STEP : (want > 4096 ? 4096 : want);
+  p.tile_tokens = (int)((want + STEP - 1) / STEP * STEP);
+  p.n_tiles = (p.sh.S + p.tile_tokens - 1) / p.tile_tokens;
   const dim3 grid((unsigned)((size_t)p.n_tiles * p.sh.B * p.sh.Hkv));
   switch (p.sh.g) {
     case 1: score_panel_kernel<DT, LPT, 1><<<grid, kScoreThreads, 0, st>>>(p); break;
