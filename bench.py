@@ -8,7 +8,10 @@ A step is the whole hot path: query rotation, low-dim scores of every cached
 token, per-(batch, head) top-k, exact attention over the selected tokens.
 Inputs are resident in HBM before timing starts; three independent copies of
 the caches are cycled so that a step never finds its data in the 256 MB
-Infinity Cache from an earlier step.
+Infinity Cache from an earlier step.  Before the W warm-up steps the step runs
+untimed for about 0.2 s (--settle) so that the clocks are at steady state.
+The timed step is the method's call loki_decode(q, Kcache_rot, V, P, d, k,
+out): the optional index output is not requested.
 
 Prints ONE JSON line.  value = algorithmic bytes per step / step time, where
 the algorithmic bytes are, per step, B*Hkv*S*d elements for scoring plus
@@ -41,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_13b_f16")
     ap.add_argument("--sets", type=int, default=3, help="independent cache copies cycled")
+    ap.add_argument("--settle", type=float, default=0.2,
+                    help="seconds of untimed steps before the warm-up (steady clocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample")
@@ -130,13 +135,15 @@ def main():
                 calls.append((loki.lib.loki_decode_append,
                               (vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
                                vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d,
-                               wl.k, vp(out.data_ptr()), vp(idx.data_ptr()), ctypes.byref(cd),
+                               wl.k, vp(out.data_ptr()), None, ctypes.byref(cd),
                                vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))))
             else:
+                # the step of the method: loki_decode(q, Kcache_rot, V, P, d, k, out);
+                # the optional index output is not requested
                 calls.append((loki.lib.loki_decode,
                               (vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
                                vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()),
-                               vp(idx.data_ptr()), ctypes.byref(cd), vp(ws.data_ptr()),
+                               None, ctypes.byref(cd), vp(ws.data_ptr()),
                                ws.numel(), vp(stream.cuda_stream))))
         return cd, calls
 
@@ -150,6 +157,17 @@ def main():
         if rc != 0:
             raise RuntimeError(f"decode failed: {loki.strerror(rc)} {loki.last_error()}")
 
+    # the device first runs the step for about args.settle seconds so that its
+    # clocks reach their steady state (a decode server runs continuously; a
+    # 20-step warm-up alone leaves the timed steps a few percent slower), then
+    # the W warm-up steps
+    t_settle = time.time()
+    i = 0
+    while time.time() - t_settle < args.settle:
+        for _ in range(50):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -89,6 +89,16 @@ typedef struct {
    results up to fp32 summation order; for profiling the phases. */
 #define LOKI_FLAG_SEPARATE_KERNELS 1u
 
+/* loki_desc.flags: in the one-launch kernel, one workgroup per (b, kv) only.
+   By default (single query head per KV head, k >= 256), when the (b, kv)
+   units do not fill whole rounds of the compute units, spare workgroup slots
+   run helpers: a helper repeats the selection of one of the units of the
+   last round and attends the second half of its rows, and the two halves are
+   merged (through the workspace).  Same index sets; outputs equal up to fp32
+   summation order.  Helpers are also off while `stream` is being captured
+   into a graph. */
+#define LOKI_FLAG_NO_HELPERS 2u
+
 /* Human-readable name of a status code; never NULL. */
 const char* loki_strerror(int status);
 

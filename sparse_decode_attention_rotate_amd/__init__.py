@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 F32, F16, BF16 = 0, 1, 2
 FLAG_SEPARATE_KERNELS = 1
+FLAG_NO_HELPERS = 2
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 NAME_CODE = {"f32": F32, "f16": F16, "bf16": BF16}

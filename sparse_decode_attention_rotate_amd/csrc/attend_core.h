@@ -162,4 +162,14 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
   }
 }
 
+// Merge of two partial results (M, L, A) of disjoint row sets of one query
+// row (log2 domain, A unnormalised): the output coordinate.
+__device__ __forceinline__ float combine_partials(float M0, float L0, float A0, float M1, float L1,
+                                                  float A1) {
+  const float M = fmaxf(M0, M1);
+  const float w0 = M0 == -INFINITY ? 0.f : exp2f(M0 - M);
+  const float w1 = M1 == -INFINITY ? 0.f : exp2f(M1 - M);
+  return fmaf(A0, w0, A1 * w1) / fmaf(L0, w0, L1 * w1);
+}
+
 }  // namespace loki

@@ -39,6 +39,24 @@ constexpr size_t kFusedDynBytes = 36 * 1024;
 #endif
 constexpr int kFusedRowsPerBatch = LOKI_FUSED_RB;  // gather rows per lane group per batch
 
+// Words exchanged between the two workgroups of a paired unit are accessed
+// only with agent-coherent loads and stores (relaxed agent-scope atomics,
+// which bypass the non-coherent caches): a workgroup waits until its stores
+// are complete before it touches the pair's flag, and reads its partner's
+// words only after the flag showed the partner had been there.  No cache
+// writeback or invalidate is needed (release / acquire fences would write
+// back or invalidate a whole L2 each time, at a cost to every workgroup on
+// that die).
+__device__ __forceinline__ void st_coherent(float* a, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(a), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* a) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(a), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
 template <int DT, int D, int LPT, int G, int NT>
 __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParams p) {
   constexpr int NW = NT / 64;
@@ -60,6 +78,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   __shared__ float qpart[NW][G][D];      // per-wave partial rotations
   __shared__ float qs[G][D];             // rotated query rows
   __shared__ float rng[2][NW][G];        // per-wave score min / max
+  __shared__ int later;                  // paired unit: this workgroup merges the halves
 
   const Shape& sh = p.sh;
   const int S = sh.S, k = p.k;
@@ -72,7 +91,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   // streaming phases of co-resident workgroups; streaming runs at the lowest.
   __builtin_amdgcn_s_setprio(3);
 
-  const size_t head = blockIdx.x;  // b * Hkv + kv
+  // The unit of this workgroup.  Workgroups past the last unit are helpers:
+  // helper j repeats the rotation, scores and top-k of unit help_first + j
+  // (same code, same data, same rows) and attends the second half of its
+  // selected rows while the unit's own workgroup attends the first half; the
+  // later of the two merges the halves.  Only single-head units are paired.
+  const bool helper = (int)blockIdx.x >= p.n_units;
+  const size_t head = helper ? (size_t)(p.help_first + ((int)blockIdx.x - p.n_units))
+                             : (size_t)blockIdx.x;  // b * Hkv + kv
+  const int pair = (int)head - p.help_first;
+  const bool paired = G == 1 && p.n_help > 0 && pair >= 0 && pair < p.n_help;
   const int b = (int)(head / sh.Hkv), kv = (int)(head % sh.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query head of the group
@@ -358,11 +386,45 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 
   __builtin_amdgcn_s_setprio(0);
   // ---- 3. exact attention over the selected tokens of each head
-  if (p.idx_out) {
-    if (stream_rows)
-      write_rows_in_index_order(sidx, ssm.sel_gt, k, p.idx_out + q0 * k, NT);
-    else
-      for (int e = tid; e < G * k; e += NT) p.idx_out[q0 * k + e] = sidx[e];
+  // (the index sets, when asked for, are written after it: off its critical path)
+  auto write_idx = [&]() {
+    if (p.idx_out && !helper) {
+      if (stream_rows)
+        write_rows_in_index_order(sidx, ssm.sel_gt, k, p.idx_out + q0 * k, NT);
+      else
+        for (int e = tid; e < G * k; e += NT) p.idx_out[q0 * k + e] = sidx[e];
+    }
+  };
+  if (paired) {
+    // owner: rows [0, k0); helper: rows [k0, k).  Partials (M, L, A[D]) of
+    // pair j: owner's at help_part[2j], helper's at help_part[2j+1].
+    const int r0 = helper ? p.k0 : 0, nr = helper ? k - p.k0 : p.k0;
+    float M, L, A;
+    block_attend<DT, D, NT, true, kFusedRowsPerBatch>(qs[0], p.scale_log2, sidx + r0, slow + r0,
+                                                      nr, p.kcache, p.vcache, head, sh, asm_, M,
+                                                      L, A);
+    float* mine = p.help_part + ((size_t)pair * 2 + (helper ? 1 : 0)) * (D + 2);
+    const float* other = p.help_part + ((size_t)pair * 2 + (helper ? 0 : 1)) * (D + 2);
+    if (tid < D) st_coherent(mine + 2 + tid, A);
+    if (tid == 0) {
+      st_coherent(mine, M);
+      st_coherent(mine + 1, L);
+    }
+    wait_stores();
+    __syncthreads();
+    if (tid == 0)
+      later = __hip_atomic_exchange(p.help_flag + pair, p.tag, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == p.tag;
+    __syncthreads();
+    if (later && tid < D) {
+      const float oM = ld_coherent(other), oL = ld_coherent(other + 1);
+      const float oA = ld_coherent(other + 2 + tid);
+      // always the owner's half first: the result does not depend on which merges
+      p.out[head * D + tid] = helper ? combine_partials(oM, oL, oA, M, L, A)
+                                     : combine_partials(M, L, A, oM, oL, oA);
+    }
+    write_idx();
+    return;
   }
   for (int h = 0; h < G; h++) {
     float M, L, A;
@@ -371,11 +433,12 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     if (tid < D) p.out[(q0 + h) * D + tid] = A / L;
     __syncthreads();  // asm_ is reused by the next head
   }
+  write_idx();
 }
 
 template <int DT, int D, int LPT, int NT>
 hipError_t launch_nt(const FusedParams& p, size_t dyn, hipStream_t st) {
-  const dim3 grid((unsigned)(p.sh.B * p.sh.Hkv));
+  const dim3 grid((unsigned)(p.n_units + p.n_help));
   switch (p.sh.g) {
     case 1: fused_kernel<DT, D, LPT, 1, NT><<<grid, NT, dyn, st>>>(p); break;
     case 2: fused_kernel<DT, D, LPT, 2, NT><<<grid, NT, dyn, st>>>(p); break;

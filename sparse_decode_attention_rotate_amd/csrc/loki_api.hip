@@ -5,7 +5,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <random>
 #include <string>
+#include <unordered_map>
 
 #include "loki.h"
 #include "loki_internal.h"
@@ -85,7 +88,7 @@ int check_desc(const loki_desc* d, Shape* sh) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qr, scores, idx, sel, part, total;
+  size_t qr, scores, idx, sel, part, help_flag, help_part, total;
   int nsplit;
 };
 
@@ -104,8 +107,39 @@ WsLayout ws_layout(const Shape& sh, int k) {
   off += align256(units * (size_t)k * 4);
   w.part = off;
   off += w.nsplit > 1 ? align256(units * w.nsplit * (size_t)(sh.D + 2) * 4) : 0;
+  // paired units of the one-launch kernel: one flag and two partials per (b, kv)
+  const size_t kv_units = (size_t)sh.B * sh.Hkv;
+  w.help_flag = off;
+  off += align256(kv_units * 8);
+  w.help_part = off;
+  off += align256(kv_units * 2 * (size_t)(sh.D + 2) * 4);
   w.total = off;
   return w;
+}
+
+// Launch tags of the paired units, per workspace: a pair's flag holds the tag
+// of the launch that last used it, so stale flags never match a later launch
+// and need no reset; a random start makes a match with whatever an earlier
+// process left in the memory unlikely (64-bit tags).
+unsigned long long next_tag(const void* workspace) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, unsigned long long> tags;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = tags.find(workspace);
+  if (it == tags.end()) {
+    std::random_device rd;
+    const unsigned long long start = ((unsigned long long)rd() << 32) ^ rd();
+    it = tags.emplace(workspace, start).first;
+  }
+  if (++it->second == 0) ++it->second;
+  return it->second;
+}
+
+// A graph replays its kernel arguments, tag included: no pairing under capture.
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &status) != hipSuccess) return true;
+  return status != hipStreamCaptureStatusNone;
 }
 
 // Compute units of the current device (cached per device).
@@ -172,7 +206,29 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     fp.sh = sh;
     // one workgroup per (b, kv): with no more of them than compute units, use
     // 512 threads so that each unit has twice the loads in flight
-    fp.threads = (long)sh.B * sh.Hkv <= compute_units() ? 512 : 256;
+    const int units = sh.B * sh.Hkv, ncu = compute_units();
+    fp.threads = units <= ncu ? 512 : 256;
+    fp.n_units = units;
+    // Paired units: when the units do not fill whole rounds of one workgroup
+    // per compute unit, the last (partial) round leaves some compute units
+    // with one unit more than the others.  Up to as many helper workgroups as
+    // that round has free slots take the second half of the attention of
+    // those units (k >= 256, single head); a multiple of 8 keeps a helper on
+    // the same die (L2) as its unit, whose panel it re-reads.
+    const int per_cu = fp.threads == 256 ? 3 : 2;  // resident workgroups per CU
+    const int full = units / ncu, part = units % ncu;
+    int n_help = 0;
+    if (sh.g == 1 && k >= 256 && part > 0 && full + 1 <= per_cu &&
+        !(desc->flags & LOKI_FLAG_NO_HELPERS) && !stream_capturing(st))
+      n_help = (part < ncu - part ? part : ncu - part) / 8 * 8;
+    fp.n_help = n_help;
+    fp.help_first = units - n_help;
+    fp.k0 = (k / 2 + 63) / 64 * 64;
+    if (n_help > 0) {
+      fp.help_part = reinterpret_cast<float*>(ws + w.help_part);
+      fp.help_flag = reinterpret_cast<unsigned long long*>(ws + w.help_flag);
+      fp.tag = next_tag(workspace);
+    }
     return hip_status(launch_fused(fp, st), "fused");
   }
 

@@ -68,6 +68,12 @@ struct FusedParams {
   int k;
   float scale_log2;
   int threads;          // workgroup size: 256 or 512
+  // paired units (single head): helpers for units [help_first, help_first + n_help)
+  int n_units;          // B * Hkv: workgroups with a unit of their own
+  int help_first, n_help, k0;
+  float* help_part;     // [n_help][2][D + 2] partials (coherent accesses only)
+  unsigned long long* help_flag;  // [n_help] launch tag of the first half done
+  unsigned long long tag;         // unique per launch on one workspace, nonzero
   Shape sh;
 };
 

@@ -449,21 +449,27 @@ __device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k,
 }
 
 // The rows of select_rows in ascending index order, to global memory: the two
-// index-ordered parts [0, n1) and [n1, k) merged by binary search (all NT
-// threads, after the rows are visible).
+// index-ordered parts [0, n1) (the members of bins above b*) and [n1, k) (the
+// taken members of b*, usually few) merged: a row of the first part moves up
+// by the taken members below it, a taken member by the first-part rows below
+// it (binary search).  All NT threads, after the rows are visible.
 __device__ __forceinline__ void write_rows_in_index_order(const int32_t* rows, int n1, int k,
                                                           int32_t* out, int NT) {
-  auto lower = [&](int from, int n, int t) {  // first position in rows[from, from+n) >= t
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (rows[from + mid] < t) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
+  const int n2 = k - n1;
   for (int r = threadIdx.x; r < k; r += NT) {
     const int t = rows[r];
-    const int pos = r < n1 ? r + lower(n1, k - n1, t) : (r - n1) + lower(0, n1, t);
+    int pos;
+    if (r < n1) {
+      pos = r;
+      for (int j = 0; j < n2; j++) pos += rows[n1 + j] < t ? 1 : 0;  // broadcast reads
+    } else {
+      int lo = 0, hi = n1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (rows[mid] < t) lo = mid + 1; else hi = mid;
+      }
+      pos = (r - n1) + lo;
+    }
     out[pos] = t;
   }
 }

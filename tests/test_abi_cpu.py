@@ -46,6 +46,14 @@ def test_library_exports_every_declared_symbol(L):
     assert set(declared) <= exported
 
 
+def test_header_flags_match_binding(L):
+    src = open(HEADER).read()
+    flags = dict(re.findall(r"#define\s+LOKI_(FLAG_\w+)\s+(\d+)u", src))
+    assert flags == {"FLAG_SEPARATE_KERNELS": "1", "FLAG_NO_HELPERS": "2"}
+    for name, v in flags.items():
+        assert getattr(L, name) == int(v)
+
+
 def _desc(L, **kw):
     base = dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, seq_len=100,
                 seq_capacity=128, panel_dim=32, dtype=L.F16)

@@ -340,6 +340,59 @@ def test_repeat_runs_are_bit_identical(L):
         assert np.array_equal(o1, o2) and np.array_equal(i1, i2)
 
 
+# ------------------------------------------- helpers (one-launch path)
+
+def _decode_with(L, wl, dev, flags, ws):
+    desc = dev["desc"].with_flags(flags)
+    idx = torch.full((wl.B, wl.Hq, wl.k), -7, dtype=torch.int32, device="cuda")
+    out = L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc, idx_out=idx,
+                   workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,B,nh,S,k", [("f16", 12, 40, 2048, 512), ("bf16", 2, 4, 3000, 333),
+                                            ("f32", 3, 8, 1500, 256)])
+def test_helpers_match_solo_units(L, dtype, B, nh, S, k):
+    """Units of a partial round shared with helper workgroups (12 x 40 units:
+    32 helpers on 256 compute units; the smaller shapes: every unit paired):
+    the solo path's index sets, its outputs up to fp32 summation order,
+    bit-identical outputs from launch to launch on one workspace, oracle parity."""
+    wl = _small(dtype, B=B, Hq=nh, Hkv=nh, S=S, k=k)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    ws = L.empty_workspace(dev["desc"], wl.d, wl.k)
+    out_solo, idx_solo = _decode_with(L, wl, dev, L.FLAG_NO_HELPERS, ws)
+    first = None
+    for rep in range(4):
+        out, idx = _decode_with(L, wl, dev, 0, ws)
+        assert np.array_equal(idx, idx_solo)
+        assert H.rel_err_rows(out, out_solo).max() < 1e-5
+        if first is None:
+            first = out
+        else:
+            assert np.array_equal(out, first), f"launch {rep} differs from launch 0"
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  helpers {dtype} B={B} heads={nh}: {res}")
+
+
+@pytest.mark.parametrize("fill", ["random", "ones"])
+def test_helpers_with_dirty_workspace(L, fill):
+    """The pair flags need no initialisation: a workspace full of garbage (or
+    of 0xff bytes) gives correct results from the first launch on."""
+    wl = _small("f16", B=2, Hq=8, Hkv=8, S=1500, k=300)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    n = L.workspace_bytes(dev["desc"], wl.d, wl.k)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    ws = (torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=g)
+          if fill == "random" else torch.full((n,), 255, dtype=torch.uint8, device="cuda"))
+    for _ in range(2):
+        out, idx = _decode_with(L, wl, dev, 0, ws)
+        res = H.full_parity(wl, x, out, idx)
+    H.log(f"  dirty workspace ({fill}): {res}")
+
+
 # ------------------------------------------------ dense decode attention
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,S", [("f16", 4, 4, 3000), ("bf16", 8, 2, 1111),
