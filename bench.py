@@ -239,6 +239,42 @@ def main():
     full_bytes = es_ * wl.B * wl.Hkv * wl.S * wl.D * 2
     del ws_full
 
+    # Exact-TopK, the pages' other baseline: scores over all D coordinates
+    # (panel = the whole rotated key row), top-k, attention over the k rows
+    exact = None
+    if not wl.append:
+        desc_x = loki.Desc(batch=wl.B, n_q_heads=wl.Hq, n_kv_heads=wl.Hkv, head_dim=wl.D,
+                           seq_len=wl.S, seq_capacity=wl.capacity, panel_dim=wl.D,
+                           dtype=loki.NAME_CODE[wl.dtype])
+        kc_x = loki.empty_kcache(desc_x)
+        loki.pack_kcache(up(x["krot"]), kc_x, desc_x.with_seq_len(wl.capacity))
+        ws_x = loki.empty_workspace(desc_x, wl.D, wl.k)
+        cdx = desc_x.c()
+        kcx_, wsx_ = vp(kc_x.data_ptr()), vp(ws_x.data_ptr())
+        chk(lib.loki_decode(q_, kcx_, vcs[0], P_, wl.D, wl.k, out_, None, ctypes.byref(cdx), wsx_,
+                            ws_x.numel(), st))
+        exact_us = timed(lambda i: lib.loki_decode(q_, kcx_, vcs[i % len(vcs)], P_, wl.D, wl.k, out_,
+                                                   None, ctypes.byref(cdx), wsx_, ws_x.numel(), st))
+        exact_bytes = es_ * (wl.B * wl.Hkv * wl.S * wl.D + wl.B * wl.Hq * wl.k * wl.D)
+        exact = {"us_per_step": round(exact_us, 2), "bytes_per_step": exact_bytes,
+                 "GBps": round(exact_bytes / (exact_us * 1e-6) / 1e9, 1),
+                 "loki_speedup": round(exact_us / (ms_per_step * 1e3), 3)}
+        del kc_x, ws_x
+
+    # prefill: the prompt's S keys of every (b, kv) projected by P into a cache
+    # copy (the kernel alone; V rows are a plain copy).  Input: stored rows of
+    # the same shape and distribution.
+    k_rows = up(x["krot"][:, :, :wl.S])
+    kc_p = loki.empty_kcache(desc)
+    kr_, kcp_ = vp(k_rows.data_ptr()), vp(kc_p.data_ptr())
+    chk(lib.loki_prefill(kr_, None, wl.S, 0, P_, kcp_, None, cd, st))
+    prefill_us = timed(lambda i: lib.loki_prefill(kr_, None, wl.S, 0, P_, kcp_, None, cd, st))
+    prefill_bytes = es_ * wl.B * wl.Hkv * wl.S * wl.D * 2
+    prefill = {"us_per_call": round(prefill_us, 2), "tokens": wl.S, "bytes_per_call": prefill_bytes,
+               "GBps": round(prefill_bytes / (prefill_us * 1e-6) / 1e9, 1),
+               "frac_hbm_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del k_rows, kc_p
+
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()
     score_bytes = es * wl.B * wl.Hkv * wl.S * wl.d
@@ -279,6 +315,8 @@ def main():
         "full_attention": {"us_per_step": round(full_us, 2), "kv_bytes_per_step": full_bytes,
                            "GBps": round(full_bytes / (full_us * 1e-6) / 1e9, 1),
                            "loki_speedup": round(full_us / (ms_per_step * 1e3), 3)},
+        "exact_topk": exact,
+        "prefill": prefill,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

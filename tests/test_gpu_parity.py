@@ -75,6 +75,14 @@ def test_rotate_query(L, dtype, Hq, Hkv):
 
 # ----------------------------------------------------------------- append
 
+def _ulp(r: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the f16 / bf16 values at |r| (subnormal spacing below the
+    smallest normal)."""
+    mant, emin = {"f16": (10, -14), "bf16": (7, -126)}[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** emin)))
+    return 2.0 ** (e - mant)
+
+
 @pytest.mark.parametrize("dtype,dp", [("f32", 32), ("f16", 32), ("bf16", 32), ("f16", 128),
                                       ("bf16", 16)])
 def test_append_row(L, dtype, dp):
@@ -99,16 +107,110 @@ def test_append_row(L, dtype, dp):
         mag = np.einsum("bhi,hij->bhj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
         assert np.all(np.abs(g - r) <= 2 * 128 * 2.0 ** -24 * mag)
     else:
-        # fp32 product rounded once to f16 / bf16: at most one unit in the last place
-        mant = {"f16": 10, "bf16": 7}[dtype]
-        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - mant)
-        assert np.all(np.abs(g - r) <= ulp)
+        # fp32 product rounded once to f16 / bf16: one unit in the last place
+        # plus the fp32 dot-product error (which matters only under cancellation)
+        kn = W.from_storage(x["k_new"], dtype)
+        mag = np.einsum("bhi,hij->bhj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
+        assert np.all(np.abs(g - r) <= _ulp(r, dtype) + 2 * 128 * 2.0 ** -24 * mag)
         assert frac_exact > 0.99
     assert np.array_equal(H.to_host(dev["v"], dtype)[:, :, pos], vr)
     # other rows untouched
     keep = np.ones(64, bool)
     keep[pos] = False
     assert np.array_equal(got[:, :, keep], x["krot"][:, :, keep])
+
+
+# ----------------------------------------------------------------- prefill
+
+def _oracle_prefill(k_rows, v_rows, P, dtype):
+    """The oracle's append applied to every token of k_rows [B, Hkv, n, D]."""
+    B, Hkv, n, D = k_rows.shape
+    kt = np.ascontiguousarray(k_rows.transpose(0, 2, 1, 3).reshape(B * n, Hkv, D))
+    vt = np.ascontiguousarray(v_rows.transpose(0, 2, 1, 3).reshape(B * n, Hkv, D))
+    kr, _ = oracle.append_rows(kt, vt, P, dtype)
+    return np.ascontiguousarray(kr.reshape(B, n, Hkv, D).transpose(0, 2, 1, 3))
+
+
+def _raw(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32 if a.dtype.itemsize == 4 else np.uint16)
+
+
+def _random_bits(g, shape, dtype):
+    bits = g.integers(0, 1 << 16, shape, dtype=np.uint32).astype(np.uint16)
+    if dtype == "f32":
+        return (bits.astype(np.uint32) * 65537).view(np.float32)
+    return bits if dtype == "bf16" else bits.view(np.float16)
+
+
+@pytest.mark.parametrize("dtype,D,dp,n,pos", [
+    ("f16", 128, 32, 1100, 37), ("bf16", 128, 16, 1100, 0), ("f32", 128, 32, 700, 5),
+    ("f16", 128, 128, 64, 0), ("bf16", 128, 64, 1, 1199), ("bf16", 128, 32, 600, 600),
+    ("f16", 64, 16, 300, 3), ("f32", 64, 8, 513, 0)])
+def test_prefill(L, dtype, D, dp, n, pos):
+    S_cap = 1200
+    wl = _small(dtype, D=D, S=n, S_cap=S_cap, Hq=3, Hkv=3, d=min(32, D), k=1)
+    H.log(f"prefill {dtype} D={D} dp={dp} n={n} pos={pos}")
+    x = W.generate(wl, with_raw_keys=True)
+    k_rows = W.to_storage(x["k64"], dtype)
+    v_rows = x["v"][:, :, :n]
+    g = np.random.default_rng(11)
+    k_init = _random_bits(g, (wl.B, wl.Hkv, S_cap, D), dtype)
+    v_init = _random_bits(g, (wl.B, wl.Hkv, S_cap, D), dtype)
+    desc = H.make_desc(wl, dp)
+    kcache = L.empty_kcache(desc)
+    L.pack_kcache(H.to_device(k_init, dtype), kcache, desc.with_seq_len(S_cap))
+    vcache = H.to_device(v_init, dtype)
+    P = torch.from_numpy(x["P"]).cuda()
+    L.prefill(H.to_device(k_rows, dtype), P, kcache, desc, v_rows=H.to_device(v_rows, dtype),
+              vcache=vcache, pos=pos)
+    rows = L.unpack_kcache(kcache, S_cap, desc.with_seq_len(S_cap))
+    torch.cuda.synchronize()
+    got = H.to_host(rows, dtype)
+    inside = np.zeros(S_cap, bool)
+    inside[pos:pos + n] = True
+    # rows outside [pos, pos + n) keep their bits, in both caches
+    assert np.array_equal(_raw(got[:, :, ~inside]), _raw(k_init[:, :, ~inside]))
+    vg = H.to_host(vcache, dtype)
+    assert np.array_equal(_raw(vg[:, :, ~inside]), _raw(v_init[:, :, ~inside]))
+    assert np.array_equal(_raw(vg[:, :, inside]), _raw(np.ascontiguousarray(v_rows)))
+    ref = _oracle_prefill(k_rows, v_rows, x["P"], dtype)
+    gk = W.from_storage(got[:, :, inside], dtype)
+    rk = W.from_storage(ref, dtype)
+    frac_exact = np.mean(gk == rk)
+    H.log(f"  elements equal to the oracle's rounding: {frac_exact:.5f}")
+    # fp32-accurate product (fp32 dot-product error bound), rounded once: for
+    # f16 / bf16 one unit in the last place more
+    kn = W.from_storage(k_rows, dtype)
+    mag = np.einsum("bhti,hij->bhtj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
+    bound = 2 * D * 2.0 ** -24 * mag + (0.0 if dtype == "f32" else _ulp(rk, dtype))
+    ratio = np.abs(gk - rk) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    H.log(f"  worst |gpu - oracle| / bound = {ratio[worst]:.3f} at {worst}: "
+          f"gpu {gk[worst]!r} oracle {rk[worst]!r} magnitude {mag[worst]:.3e}")
+    assert np.all(ratio <= 1.0)
+    if dtype != "f32":
+        assert frac_exact > 0.99
+
+
+@pytest.mark.parametrize("dtype,g", [("f16", 4), ("bf16", 1)])
+def test_prefill_then_decode(L, dtype, g):
+    """A cache filled by loki_prefill decodes like the oracle's own prefill."""
+    wl = _small(dtype, B=2, Hq=2 * g, Hkv=2, S=2500, S_cap=2600, d=32, k=256)
+    H.log(f"prefill + decode {dtype} g={g}")
+    x = W.generate(wl, with_raw_keys=True)
+    k_rows = W.to_storage(x["k64"], dtype)
+    desc = H.make_desc(wl, 32)
+    dev = {"desc": desc, "q": H.to_device(x["q"], dtype), "P": torch.from_numpy(x["P"]).cuda(),
+           "kcache": L.empty_kcache(desc), "v": torch.zeros((wl.B, wl.Hkv, 2600, wl.D),
+                                                           dtype=desc.torch_dtype, device="cuda")}
+    L.prefill(H.to_device(k_rows, dtype), dev["P"], dev["kcache"], desc,
+              v_rows=H.to_device(np.ascontiguousarray(x["v"][:, :, :wl.S]), dtype),
+              vcache=dev["v"])
+    out, idx = H.run_decode(wl, dev)
+    krot = np.zeros_like(x["krot"])
+    krot[:, :, :wl.S] = _oracle_prefill(k_rows, x["v"][:, :, :wl.S], x["P"], dtype)
+    res = H.full_parity(wl, dict(x, krot=krot), out, idx)
+    H.log(f"  {res}")
 
 
 # ------------------------------------------------------------------ scores
@@ -409,6 +511,21 @@ def test_full_attention(L, dtype, Hq, Hkv, S):
     out = out.cpu().numpy().astype(np.float64)
     ref = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.D, S, dtype)["out"]
     assert H.rel_err_rows(out, ref).max() < H.OUT_TOL[dtype]
+
+
+# ------------------------------------------------------------- Exact-TopK
+
+@pytest.mark.parametrize("dtype,g", [("f16", 1), ("bf16", 4)])
+def test_exact_topk_full_panel(L, dtype, g):
+    """The pages' Exact-TopK baseline: panel_dim = d = D, so the selection
+    ranks the exact scores q . k_t and the attention reuses them."""
+    wl = _small(dtype, B=2, Hq=4 * g if g > 1 else 4, Hkv=4, S=2500, k=300, d=128)
+    H.log(f"exact top-k {dtype} g={g}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x, dp=128)
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {res}")
 
 
 # ---------------------------------------------------- the five workloads
