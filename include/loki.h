@@ -40,8 +40,8 @@
  *            block of S_cap*D elements, first the leading dp coordinates of
  *            every token ([S_cap, dp], token-major), then the remaining D-dp
  *            coordinates ([S_cap, D-dp]).  Same size as a row-major cache.
- *            Written only through loki_pack_kcache, loki_append and
- *            loki_decode_append.
+ *            Written only through loki_pack_kcache, loki_prefill,
+ *            loki_append and loki_decode_append.
  *   P        [Hkv, D, D] fp32 row-major; column j is the j-th principal
  *            direction (descending variance), so k_rot = k . P.  Query head h
  *            uses P[h / (Hq/Hkv)].
@@ -138,6 +138,23 @@ int loki_unpack_kcache(const void* kcache, int32_t n_tokens, void* krot_rows,
  */
 int loki_append(const void* k_new, const void* v_new, const float* P, void* kcache,
                 void* vcache, int32_t pos, const loki_desc* desc, void* stream);
+
+/*
+ * Prefill [C], [F1]: the append of a whole run of tokens at once.  For
+ * t < n_tokens, K cache row pos + t := round_to_dtype(k_rows[b,kv,t,:] . P[kv])
+ * and, when v_rows is not NULL, V cache row pos + t := v_rows[b,kv,t,:]
+ * (copied; vcache is then required).  k_rows, v_rows [B, Hkv, n_tokens, D] in
+ * the storage dtype, unrotated; 0 <= pos, pos + n_tokens <= S_cap
+ * (n_tokens = 0: nothing is enqueued).  The product is formed with fp32
+ * accuracy: fp32 keys use fp32 arithmetic; fp16 / bf16 keys use matrix-core
+ * products of the exact 16-bit keys with P split into two (fp16) or three
+ * (bf16) 16-bit parts, accumulated in fp32.  Either way the stored value is
+ * within one unit in the last place of the exact product rounded once.
+ * Rows outside [pos, pos + n_tokens) are not touched.  k_rows must not
+ * overlap the caches.
+ */
+int loki_prefill(const void* k_rows, const void* v_rows, int32_t n_tokens, int32_t pos,
+                 const float* P, void* kcache, void* vcache, const loki_desc* desc, void* stream);
 
 /* Query rotation [F1]: qr[b,h,:] = q[b,h,:] . P[h / (Hq/Hkv)] in fp32. */
 int loki_rotate_query(const void* q, const float* P, float* qr, const loki_desc* desc,

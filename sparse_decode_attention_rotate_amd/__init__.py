@@ -39,7 +39,7 @@ STATUS = {0: "LOKI_OK", -1: "LOKI_EINVAL", -2: "LOKI_EUNSUPPORTED", -3: "LOKI_EW
 EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_workspace_bytes",
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
-           "loki_decode_plan", "loki_full_attention"]
+           "loki_decode_plan", "loki_full_attention", "loki_prefill"]
 
 
 class _CDesc(ctypes.Structure):
@@ -69,6 +69,7 @@ _SIG = {
                            _i),
     "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
     "loki_full_attention": ([_vp, _vp, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
+    "loki_prefill": ([_vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _D, _vp], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(_lib, _name)
@@ -199,6 +200,22 @@ def append(k_new, v_new, P, kcache, vcache, pos: int, desc: Desc, stream=None):
     _expect(P, (desc.n_kv_heads, desc.head_dim, desc.head_dim), torch.float32, "P")
     _check(_lib.loki_append(_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(kcache), _ptr(vcache), pos,
                             ctypes.byref(desc.c()), _stream(stream)), "loki_append")
+
+
+def prefill(k_rows, P, kcache, desc: Desc, v_rows=None, vcache=None, pos: int = 0,
+            stream=None):
+    """Project a run of unrotated keys [B, Hkv, n, D] by P into K cache rows
+    [pos, pos + n); with v_rows, copy them into the same rows of vcache."""
+    n = k_rows.shape[2] if k_rows.dim() == 4 else -1
+    shp = (desc.batch, desc.n_kv_heads, n, desc.head_dim)
+    _expect(k_rows, shp, desc.torch_dtype, "k_rows")
+    if v_rows is not None:
+        _expect(v_rows, shp, desc.torch_dtype, "v_rows")
+    _expect(P, (desc.n_kv_heads, desc.head_dim, desc.head_dim), torch.float32, "P")
+    _check(_lib.loki_prefill(_ptr(k_rows), _ptr(v_rows), n, pos, _ptr(P), _ptr(kcache),
+                             _ptr(vcache), ctypes.byref(desc.c()), _stream(stream)),
+           "loki_prefill")
+    return kcache
 
 
 def rotate_query(q, P, desc: Desc, qr=None, stream=None):

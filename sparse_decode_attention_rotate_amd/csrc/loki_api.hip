@@ -376,6 +376,37 @@ int loki_append(const void* k_new, const void* v_new, const float* P, void* kcac
   return hip_status(launch_project(pp, (hipStream_t)stream), "append");
 }
 
+int loki_prefill(const void* k_rows, const void* v_rows, int32_t n_tokens, int32_t pos,
+                 const float* P, void* kcache, void* vcache, const loki_desc* desc, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(k_rows);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(kcache);
+  if (v_rows) REQUIRE_PTR(vcache);
+  if (n_tokens < 0 || pos < 0 || (int64_t)pos + n_tokens > sh.S_cap)
+    return fail(LOKI_EINVAL, "rows [%d, %d + %d) outside [0, %d)", pos, pos, n_tokens, sh.S_cap);
+  if (n_tokens == 0) return LOKI_OK;
+  hipStream_t st = (hipStream_t)stream;
+  PrefillParams pp{};
+  pp.k_rows = k_rows;
+  pp.P = P;
+  pp.kcache = kcache;
+  pp.n_tokens = n_tokens;
+  pp.pos = pos;
+  pp.sh = sh;
+  rc = hip_status(launch_prefill(pp, st), "prefill");
+  if (rc || !v_rows) return rc;
+  // V rows are stored as given: one strided copy of B*Hkv blocks of n_tokens rows
+  const size_t row = (size_t)sh.D * elem_bytes(sh.dtype);
+  return hip_status(hipMemcpy2DAsync(static_cast<char*>(vcache) + (size_t)pos * row,
+                                     (size_t)sh.S_cap * row, v_rows, (size_t)n_tokens * row,
+                                     (size_t)n_tokens * row, (size_t)sh.B * sh.Hkv,
+                                     hipMemcpyDeviceToDevice, st),
+                    "prefill V copy");
+}
+
 int loki_rotate_query(const void* q, const float* P, float* qr, const loki_desc* desc,
                       void* stream) {
   Shape sh;

@@ -77,6 +77,14 @@ struct FusedParams {
   Shape sh;
 };
 
+struct PrefillParams {
+  const void* k_rows;  // [B, Hkv, n_tokens, D] storage dtype, unrotated keys
+  const float* P;      // [Hkv, D, D]
+  void* kcache;        // split-panel layout, rows [pos, pos + n_tokens) written
+  int n_tokens, pos;
+  Shape sh;
+};
+
 struct LayoutParams {
   const void* src;
   void* dst;
@@ -90,6 +98,7 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st);
 hipError_t launch_attend(const AttendParams& p, hipStream_t st);
 hipError_t launch_layout(const LayoutParams& p, hipStream_t st);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t st);
 
 // One-launch decode step (rotation, scores, top-k, attention) for shapes whose
 // per-unit scores fit the workgroup's LDS budget.

@@ -1,0 +1,256 @@
+// Bulk projection of prompt keys into the rotated key cache.
+//
+// Loki (poster page, "Visual Insights", Figure 1 right): keys are kept in the
+// basis of the principal components found offline; a decode step appends
+// one key projected by P (poster page, "Loki's Computational Cost").  Prefill
+// does the same for a whole prompt: krot[b,kv,t,:] = k[b,kv,t,:] . P[kv] for
+// t < n_tokens, rounded once to nearest-even into the storage dtype and written
+// into the split-panel layout at rows pos + t -- a dense [n_tokens x D] . [D x D] product per
+// (b, kv).
+//
+// fp16 / bf16 keys, D = 128: MFMA 16x16x32 with fp32 accumulation.  The keys
+// are exact in their 16-bit type; P is split into parts of that type,
+// P = P_1 + P_2 (fp16, of 1024 * P so that the low part stays clear of the
+// fp16 subnormals; the factor is a power of two and divides out exactly) or
+// P_1 + P_2 + P_3 (bf16), carrying 22 / 24 significant bits like the fp32
+// product of the decode-time append.  Each wave owns 32 output coordinates and
+// keeps the parts of those columns of P[kv] in registers; a workgroup walks
+// tiles of 64 tokens through LDS (key tile in, rounded output tile out, both
+// 16-byte chunks), with the next tile's loads in flight during the products.
+// fp32 keys and D = 64 use a VALU kernel: a thread keeps one column of P in
+// registers and forms that coordinate for a run of tokens staged in LDS.
+#include "loki_internal.h"
+
+namespace loki {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPreThreads = 256;
+constexpr int kPreTile = 64;            // tokens per LDS tile
+constexpr int kPreTokensPerWG = 512;    // 8 tiles per workgroup
+
+template <int DT> struct Split;
+template <> struct Split<F16> {
+  static constexpr int N = 2;
+  static constexpr float kScale = 1024.f;
+};
+template <> struct Split<BF16> {
+  static constexpr int N = 3;
+  static constexpr float kScale = 1.f;
+};
+
+// x rounded to nearest-even in the 16-bit type: bit pattern; *back = its value
+template <int DT>
+__device__ __forceinline__ unsigned round16(float x, float* back) {
+  if constexpr (DT == F16) {
+    const _Float16 h = (_Float16)x;
+    *back = (float)h;
+    return __builtin_bit_cast(unsigned short, h);
+  } else {
+    unsigned u = __float_as_uint(x), r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      r = (u >> 16) | 0x40u;  // quiet NaN
+    } else {
+      u += 0x7fffu + ((u >> 16) & 1u);
+      r = u >> 16;
+    }
+    *back = __uint_as_float(r << 16);
+    return r;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float4_t mfma32(u32x4 a, u32x4 b, float4_t c) {
+  if constexpr (DT == F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Operand layout of the 16x16x32 product (64 lanes): lane l supplies row l%16
+// of A and column l%16 of B, each at the 8 inner indices 8*(l/16) .. +7 of the
+// 32-wide step; result element i of lane l is row 4*(l/16)+i, column l%16.
+template <int DT>
+__global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillParams p) {
+  constexpr int D = 128, NS = Split<DT>::N, KSTEPS = D / 32, TB = kPreTile / 16;
+  constexpr int RP = D + 8;  // padded LDS row (16-bit elements): 272 bytes
+  __shared__ __align__(16) unsigned short kt[kPreTile][RP];
+  __shared__ __align__(16) unsigned short ot[kPreTile][RP];
+
+  const Shape& sh = p.sh;
+  const size_t head = blockIdx.y;
+  const int kv = (int)(head % sh.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane % 16, kg = lane / 16;
+
+  const int t_begin = blockIdx.x * kPreTokensPerWG;
+  const int t_end = min(p.n_tokens, t_begin + kPreTokensPerWG);
+  const unsigned short* krow =
+      static_cast<const unsigned short*>(p.k_rows) + head * (size_t)p.n_tokens * D;
+  // a tile = 64 tokens x 16 chunks of 16 bytes; thread tid moves chunks tid + 256u
+  auto load_tile = [&](u32x4 (&x)[4], int t0) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = tid + u * kPreThreads, t = t0 + c / 16;
+      x[u] = t < t_end ? *reinterpret_cast<const u32x4*>(krow + (size_t)t * D + (c % 16) * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 xk[4];
+  load_tile(xk, t_begin);
+
+  // parts of columns [32w, 32w+32) of P[kv]: bp[s][cb][ks] holds rows
+  // 32ks + 8kg .. +7 of column 32w + 16cb + n
+  u32x4 bp[NS][2][KSTEPS];
+  {
+    const float* P = p.P + (size_t)kv * D * D;
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ks++) {
+        unsigned bits[NS][8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          float r = P[(size_t)(32 * ks + 8 * kg + j) * D + 32 * wave + 16 * cb + n] * Split<DT>::kScale;
+#pragma unroll
+          for (int s = 0; s < NS; s++) {
+            float v;
+            bits[s][j] = round16<DT>(r, &v);
+            r -= v;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+          bp[s][cb][ks] = u32x4{bits[s][0] | (bits[s][1] << 16), bits[s][2] | (bits[s][3] << 16),
+                                bits[s][4] | (bits[s][5] << 16), bits[s][6] | (bits[s][7] << 16)};
+      }
+  }
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kPreTile) {
+    // kt is free: every wave passed the previous tile's second barrier after
+    // its last read of kt
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = tid + u * kPreThreads;
+      *reinterpret_cast<u32x4*>(&kt[c / 16][(c % 16) * 8]) = xk[u];
+    }
+    if (t0 + kPreTile < t_end) load_tile(xk, t0 + kPreTile);
+    __syncthreads();
+
+    float4_t acc[TB][2];
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++) acc[tb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++)
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[16 * tb + n][32 * ks + 8 * kg]);
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+          for (int s = 0; s < NS; s++) acc[tb][cb] = mfma32<DT>(a, bp[s][cb][ks], acc[tb][cb]);
+      }
+    // ot is free: the previous tile's reads of ot came before this barrier
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float v;
+          ot[16 * tb + 4 * kg + i][32 * wave + 16 * cb + n] =
+              (unsigned short)round16<DT>(acc[tb][cb][i] * (1.f / Split<DT>::kScale), &v);
+        }
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = tid + u * kPreThreads, tt = c / 16, j0 = (c % 16) * 8, t = t0 + tt;
+      if (t < t_end) {
+        const size_t row = (size_t)(p.pos + t);
+        const size_t e0 = j0 < sh.dp ? row * sh.dp + j0
+                                     : sh.kl.rest_off + row * sh.kl.rest + (j0 - sh.dp);
+        *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(p.kcache) + head * sh.kl.head_elems +
+                                  e0) = *reinterpret_cast<const u32x4*>(&ot[tt][j0]);
+      }
+    }
+  }
+}
+
+// Thread (slot, j) keeps column j of P[kv] in registers and forms coordinate j
+// of tokens slot, slot + NSLOT, ... of each run of RUN tokens staged in LDS.
+template <int DT, int D>
+__global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams p) {
+  constexpr int NSLOT = kPreThreads / D, RUN = 32;
+  __shared__ __align__(16) float xs[RUN][D];
+  const Shape& sh = p.sh;
+  const size_t head = blockIdx.y;
+  const int kv = (int)(head % sh.Hkv);
+  const int j = threadIdx.x % D, slot = threadIdx.x / D;
+  float pc[D];
+  {
+    const float* P = p.P + (size_t)kv * D * D;
+#pragma unroll
+    for (int i = 0; i < D; i++) pc[i] = P[(size_t)i * D + j];
+  }
+  const int t_begin = blockIdx.x * kPreTokensPerWG;
+  const int t_end = min(p.n_tokens, t_begin + kPreTokensPerWG);
+  for (int t0 = t_begin; t0 < t_end; t0 += RUN) {
+    __syncthreads();  // previous run consumed
+    for (int e = threadIdx.x; e < RUN * D; e += kPreThreads) {
+      const int t = t0 + e / D;
+      xs[e / D][e % D] = t < t_end ? load_elem<DT>(p.k_rows, (head * p.n_tokens + t) * D + e % D) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int r = slot; r < RUN && t0 + r < t_end; r += NSLOT) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&xs[r][i]);
+        a = fmaf(x.x, pc[i], a);
+        a = fmaf(x.y, pc[i + 1], a);
+        a = fmaf(x.z, pc[i + 2], a);
+        a = fmaf(x.w, pc[i + 3], a);
+      }
+      store_elem<DT>(p.kcache, sh.kl.at(head, (size_t)(p.pos + t0 + r), j), a);
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_dt(const PrefillParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((p.n_tokens + kPreTokensPerWG - 1) / kPreTokensPerWG),
+                  (unsigned)(p.sh.B * p.sh.Hkv));
+  if constexpr (DT != F32) {
+    if (p.sh.D == 128) {
+      prefill_mfma_kernel<DT><<<grid, kPreThreads, 0, st>>>(p);
+      return hipGetLastError();
+    }
+  }
+  if (p.sh.D == 128)
+    prefill_valu_kernel<DT, 128><<<grid, kPreThreads, 0, st>>>(p);
+  else
+    prefill_valu_kernel<DT, 64><<<grid, kPreThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t st) {
+  switch (p.sh.dtype) {
+    case F32: return launch_dt<F32>(p, st);
+    case F16: return launch_dt<F16>(p, st);
+    default: return launch_dt<BF16>(p, st);
+  }
+}
+
+}  // namespace loki

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for n in ["loki_decode", "loki_decode_append", "loki_append", "loki_rotate_query",
               "loki_score", "loki_topk", "loki_attend", "loki_pack_kcache", "loki_unpack_kcache",
               "loki_workspace_bytes", "loki_kcache_elems", "loki_strerror", "loki_last_error",
-              "loki_decode_plan", "loki_full_attention"]:
+              "loki_decode_plan", "loki_full_attention", "loki_prefill"]:
         assert n in names
 
 
@@ -137,6 +137,16 @@ def test_other_entry_points_validate(L):
     assert fa(odd, fake, fake, fake, fake, cd, fake, 1 << 30, None) == -1   # misaligned q
     assert fa(fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == -1  # desc NULL
     assert fa(fake, fake, fake, fake, fake, cd, fake, 16, None) == -3       # workspace
+    pf = lib.loki_prefill
+    assert pf(fake, None, 129, 0, fake, fake, None, cd, None) == -1     # past S_cap
+    assert pf(fake, None, 100, 29, fake, fake, None, cd, None) == -1    # pos + n past S_cap
+    assert pf(fake, None, -1, 0, fake, fake, None, cd, None) == -1
+    assert pf(fake, None, 4, -1, fake, fake, None, cd, None) == -1
+    assert pf(None, None, 4, 0, fake, fake, None, cd, None) == -1       # k_rows NULL
+    assert pf(fake, fake, 4, 0, fake, fake, None, cd, None) == -1       # v_rows without vcache
+    assert pf(fake, None, 4, 0, fake, odd, None, cd, None) == -1        # misaligned cache
+    assert pf(fake, None, 4, 0, fake, fake, None, None, None) == -1     # desc NULL
+    assert pf(fake, fake, 0, 128, fake, fake, fake, cd, None) == 0      # empty: nothing to do
 
 
 def test_binding_has_no_cpu_path(L):
