@@ -270,10 +270,15 @@ def main():
     chk(lib.loki_prefill(kr_, None, wl.S, 0, P_, kcp_, None, cd, st))
     prefill_us = timed(lambda i: lib.loki_prefill(kr_, None, wl.S, 0, P_, kcp_, None, cd, st))
     prefill_bytes = es_ * wl.B * wl.Hkv * wl.S * wl.D * 2
+    # the same bytes moved by a plain device copy: the read+write ceiling
+    cp_dst = torch.empty_like(k_rows)
+    copy_us = timed(lambda i: cp_dst.copy_(k_rows))
     prefill = {"us_per_call": round(prefill_us, 2), "tokens": wl.S, "bytes_per_call": prefill_bytes,
                "GBps": round(prefill_bytes / (prefill_us * 1e-6) / 1e9, 1),
-               "frac_hbm_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    del k_rows, kc_p
+               "frac_hbm_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+               "copy_same_bytes_us": round(copy_us, 2),
+               "frac_of_copy_rate": round(copy_us / prefill_us, 4)}
+    del k_rows, kc_p, cp_dst
 
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()

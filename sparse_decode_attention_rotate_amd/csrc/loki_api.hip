@@ -395,6 +395,7 @@ int loki_prefill(const void* k_rows, const void* v_rows, int32_t n_tokens, int32
   pp.kcache = kcache;
   pp.n_tokens = n_tokens;
   pp.pos = pos;
+  pp.cus = compute_units();
   pp.sh = sh;
   rc = hip_status(launch_prefill(pp, st), "prefill");
   if (rc || !v_rows) return rc;

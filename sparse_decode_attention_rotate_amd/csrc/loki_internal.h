@@ -82,6 +82,7 @@ struct PrefillParams {
   const float* P;      // [Hkv, D, D]
   void* kcache;        // split-panel layout, rows [pos, pos + n_tokens) written
   int n_tokens, pos;
+  int cus;             // compute units of the device
   Shape sh;
 };
 

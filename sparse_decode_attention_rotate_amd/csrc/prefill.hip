@@ -29,9 +29,11 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPreThreads = 256;
+constexpr int kPreThreads = 256;        // VALU kernel
 constexpr int kPreTile = 64;            // tokens per LDS tile
-constexpr int kPreTokensPerWG = 512;    // 8 tiles per workgroup
+constexpr int kPreTokensPerWG = 512;    // tokens per workgroup (VALU kernel)
+constexpr int kPreWaves = 8;            // MFMA kernel: waves per workgroup
+constexpr int kPreDepth = 2;            // MFMA kernel: key tiles in flight
 
 template <int DT> struct Split;
 template <> struct Split<F16> {
@@ -76,9 +78,12 @@ __device__ __forceinline__ float4_t mfma32(u32x4 a, u32x4 b, float4_t c) {
 // Operand layout of the 16x16x32 product (64 lanes): lane l supplies row l%16
 // of A and column l%16 of B, each at the 8 inner indices 8*(l/16) .. +7 of the
 // 32-wide step; result element i of lane l is row 4*(l/16)+i, column l%16.
-template <int DT>
-__global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillParams p) {
+// NW waves, each owning D/NW output coordinates (CB blocks of 16); DEPTH key
+// tiles in flight (register buffers) ahead of the one in LDS.
+template <int DT, int NW, int DEPTH, int TPWG>
+__global__ __launch_bounds__(64 * NW, 1024 / (64 * NW)) void prefill_mfma_kernel(PrefillParams p) {
   constexpr int D = 128, NS = Split<DT>::N, KSTEPS = D / 32, TB = kPreTile / 16;
+  constexpr int NT = 64 * NW, CB = D / (16 * NW), CPT = kPreTile * 16 / NT;  // chunks per thread
   constexpr int RP = D + 8;  // padded LDS row (16-bit elements): 272 bytes
   __shared__ __align__(16) unsigned short kt[kPreTile][RP];
   __shared__ __align__(16) unsigned short ot[kPreTile][RP];
@@ -88,36 +93,38 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillPar
   const int kv = (int)(head % sh.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane % 16, kg = lane / 16;
+  const int col0 = wave * 16 * CB;
 
-  const int t_begin = blockIdx.x * kPreTokensPerWG;
-  const int t_end = min(p.n_tokens, t_begin + kPreTokensPerWG);
+  const int t_begin = blockIdx.x * TPWG;
+  const int t_end = min(p.n_tokens, t_begin + TPWG);
   const unsigned short* krow =
       static_cast<const unsigned short*>(p.k_rows) + head * (size_t)p.n_tokens * D;
-  // a tile = 64 tokens x 16 chunks of 16 bytes; thread tid moves chunks tid + 256u
-  auto load_tile = [&](u32x4 (&x)[4], int t0) {
+  // a tile = 64 tokens x 16 chunks of 16 bytes; thread tid moves chunks tid + NT*u
+  auto load_tile = [&](u32x4 (&x)[CPT], int t0) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int c = tid + u * kPreThreads, t = t0 + c / 16;
+    for (int u = 0; u < CPT; u++) {
+      const int c = tid + u * NT, t = t0 + c / 16;
       x[u] = t < t_end ? *reinterpret_cast<const u32x4*>(krow + (size_t)t * D + (c % 16) * 8)
                        : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  u32x4 xk[4];
-  load_tile(xk, t_begin);
+  u32x4 xk[DEPTH][CPT];
+#pragma unroll
+  for (int b = 0; b < DEPTH; b++) load_tile(xk[b], t_begin + b * kPreTile);
 
-  // parts of columns [32w, 32w+32) of P[kv]: bp[s][cb][ks] holds rows
-  // 32ks + 8kg .. +7 of column 32w + 16cb + n
-  u32x4 bp[NS][2][KSTEPS];
+  // parts of this wave's columns of P[kv]: bp[s][cb][ks] holds rows
+  // 32ks + 8kg .. +7 of column col0 + 16cb + n
+  u32x4 bp[NS][CB][KSTEPS];
   {
     const float* P = p.P + (size_t)kv * D * D;
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ks++) {
         unsigned bits[NS][8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-          float r = P[(size_t)(32 * ks + 8 * kg + j) * D + 32 * wave + 16 * cb + n] * Split<DT>::kScale;
+          float r = P[(size_t)(32 * ks + 8 * kg + j) * D + col0 + 16 * cb + n] * Split<DT>::kScale;
 #pragma unroll
           for (int s = 0; s < NS; s++) {
             float v;
@@ -132,29 +139,30 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillPar
       }
   }
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kPreTile) {
+  // one tile: its keys (in registers) through LDS, products, rounded output
+  auto tile = [&](u32x4 (&x)[CPT], int t0) {
     // kt is free: every wave passed the previous tile's second barrier after
     // its last read of kt
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int c = tid + u * kPreThreads;
-      *reinterpret_cast<u32x4*>(&kt[c / 16][(c % 16) * 8]) = xk[u];
+    for (int u = 0; u < CPT; u++) {
+      const int c = tid + u * NT;
+      *reinterpret_cast<u32x4*>(&kt[c / 16][(c % 16) * 8]) = x[u];
     }
-    if (t0 + kPreTile < t_end) load_tile(xk, t0 + kPreTile);
+    if (t0 + DEPTH * kPreTile < t_end) load_tile(x, t0 + DEPTH * kPreTile);
     __syncthreads();
 
-    float4_t acc[TB][2];
+    float4_t acc[TB][CB];
 #pragma unroll
     for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++) acc[tb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; cb++) acc[tb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ks++)
 #pragma unroll
       for (int tb = 0; tb < TB; tb++) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[16 * tb + n][32 * ks + 8 * kg]);
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++)
+        for (int cb = 0; cb < CB; cb++)
 #pragma unroll
           for (int s = 0; s < NS; s++) acc[tb][cb] = mfma32<DT>(a, bp[s][cb][ks], acc[tb][cb]);
       }
@@ -162,18 +170,18 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillPar
 #pragma unroll
     for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++)
+      for (int cb = 0; cb < CB; cb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           float v;
-          ot[16 * tb + 4 * kg + i][32 * wave + 16 * cb + n] =
+          ot[16 * tb + 4 * kg + i][col0 + 16 * cb + n] =
               (unsigned short)round16<DT>(acc[tb][cb][i] * (1.f / Split<DT>::kScale), &v);
         }
     __syncthreads();
 
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int c = tid + u * kPreThreads, tt = c / 16, j0 = (c % 16) * 8, t = t0 + tt;
+    for (int u = 0; u < CPT; u++) {
+      const int c = tid + u * NT, tt = c / 16, j0 = (c % 16) * 8, t = t0 + tt;
       if (t < t_end) {
         const size_t row = (size_t)(p.pos + t);
         const size_t e0 = j0 < sh.dp ? row * sh.dp + j0
@@ -182,6 +190,12 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_mfma_kernel(PrefillPar
                                   e0) = *reinterpret_cast<const u32x4*>(&ot[tt][j0]);
       }
     }
+  };
+
+  for (int t0 = t_begin; t0 < t_end; t0 += DEPTH * kPreTile) {
+#pragma unroll
+    for (int b = 0; b < DEPTH; b++)
+      if (t0 + b * kPreTile < t_end) tile(xk[b], t0 + b * kPreTile);
   }
 }
 
@@ -226,16 +240,51 @@ __global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams
   }
 }
 
+template <int DT, int TPWG>
+hipError_t launch_mfma(const PrefillParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((p.n_tokens + TPWG - 1) / TPWG), (unsigned)(p.sh.B * p.sh.Hkv));
+  prefill_mfma_kernel<DT, kPreWaves, kPreDepth, TPWG><<<grid, 64 * kPreWaves, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+// Tokens per workgroup: the largest of 4096 .. 512 whose whole rounds of
+// resident workgroups (a last partial round costs as much as a full one)
+// take least time, each workgroup costing its tokens plus a set-up of about
+// 128 tokens' worth (loading and splitting its columns of P).
+template <int DT>
+hipError_t launch_mfma_sized(const PrefillParams& p, hipStream_t st) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, prefill_mfma_kernel<DT, kPreWaves, kPreDepth, 1024>, 64 * kPreWaves, 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  const long long slots = (long long)per_cu * (p.cus > 0 ? p.cus : 256);
+  const long long heads = (long long)p.sh.B * p.sh.Hkv;
+  int best = 0;
+  long long best_cost = 0;
+  for (int t : {4096, 2048, 1024, 512}) {
+    const long long wgs = (p.n_tokens + t - 1) / t * heads;
+    const long long cost = (wgs + slots - 1) / slots * (t + 128);
+    if (best == 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  switch (best) {
+    case 4096: return launch_mfma<DT, 4096>(p, st);
+    case 2048: return launch_mfma<DT, 2048>(p, st);
+    case 1024: return launch_mfma<DT, 1024>(p, st);
+    default: return launch_mfma<DT, 512>(p, st);
+  }
+}
+
 template <int DT>
 hipError_t launch_dt(const PrefillParams& p, hipStream_t st) {
+  if constexpr (DT != F32) {
+    if (p.sh.D == 128) return launch_mfma_sized<DT>(p, st);
+  }
   const dim3 grid((unsigned)((p.n_tokens + kPreTokensPerWG - 1) / kPreTokensPerWG),
                   (unsigned)(p.sh.B * p.sh.Hkv));
-  if constexpr (DT != F32) {
-    if (p.sh.D == 128) {
-      prefill_mfma_kernel<DT><<<grid, kPreThreads, 0, st>>>(p);
-      return hipGetLastError();
-    }
-  }
   if (p.sh.D == 128)
     prefill_valu_kernel<DT, 128><<<grid, kPreThreads, 0, st>>>(p);
   else

@@ -213,6 +213,38 @@ def test_prefill_then_decode(L, dtype, g):
     H.log(f"  {res}")
 
 
+@pytest.mark.parametrize("name", ["llama2_13b_f16", "gqa_llama3_8b_bf16"])
+def test_prefill_full_size(L, name):
+    """Full-size prefill (launch sizes as timed), checked on sampled token rows."""
+    wl = W.get(name)
+    dtype, B, Hkv, S, D = wl.dtype, wl.B, wl.Hkv, wl.S, wl.D
+    H.log(f"prefill full size {name}")
+    g = np.random.default_rng(2024)
+    P = np.stack([W.basis(wl, kv).astype(np.float32) for kv in range(Hkv)])
+    desc = H.make_desc(wl, 32)
+    k_dev = torch.empty((B, Hkv, S, D), dtype=desc.torch_dtype, device="cuda")
+    # seeded keys, generated on the host one batch row at a time
+    for b in range(B):
+        kb = W.to_storage(g.standard_normal((Hkv, S, D)) * W.sigma(wl)[None, None, :], dtype)
+        k_dev[b].copy_(H.to_device(kb, dtype))
+    kcache = L.empty_kcache(desc)
+    L.prefill(k_dev, torch.from_numpy(P).cuda(), kcache, desc)
+    rows = L.unpack_kcache(kcache, S, desc)
+    bs = torch.from_numpy(g.integers(0, B, 512)).cuda()
+    ts = torch.from_numpy(g.integers(0, S, 512)).cuda()
+    got = H.to_host(rows[bs, :, ts].contiguous(), dtype)     # [512, Hkv, D]
+    k_in = H.to_host(k_dev[bs, :, ts].contiguous(), dtype)
+    torch.cuda.synchronize()
+    kr, _ = oracle.append_rows(k_in, k_in, P, dtype)
+    gk, rk = W.from_storage(got, dtype), W.from_storage(kr, dtype)
+    mag = np.einsum("nhi,hij->nhj", np.abs(W.from_storage(k_in, dtype)), np.abs(P.astype(np.float64)))
+    bound = 2 * D * 2.0 ** -24 * mag + _ulp(rk, dtype)
+    frac_exact = np.mean(gk == rk)
+    H.log(f"  sampled elements equal to the oracle's rounding: {frac_exact:.5f}")
+    assert np.all(np.abs(gk - rk) <= bound)
+    assert frac_exact > 0.99
+
+
 # ------------------------------------------------------------------ scores
 
 @pytest.mark.parametrize("dtype,g,d,dp", [("f16", 1, 32, 32), ("bf16", 4, 32, 32),
