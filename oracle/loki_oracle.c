@@ -408,6 +408,67 @@ int oracle_attend_given(int B, int Hq, int Hkv, int S, int D, int k, double scal
 }
 
 /*
+ * PCAAttn, the variant of Loki that uses the low-dimensional attention scores
+ * directly (poster page, "More on tables", the PCAAttn table, which describes
+ * it as a Loki variant working with the reduced-dimensional scores).  Reading:
+ * no top-k; each cached token's logit is scale times its low-dimensional score
+ * (the dot product over the leading d rotated coordinates, as in the decode
+ * step), softmax runs over all S tokens and the output is the weighted sum of
+ * all S value rows.  Arguments as oracle_decode (out [B,Hq,D] only).
+ */
+int oracle_pca_attention(int B, int Hq, int Hkv, int S, int D, int d, double scale, int dtype,
+                         const void *q, const void *krot, const void *v, const double *P,
+                         const int32_t *heads, int n_heads, double *out)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || D < 1 || d < 1 || d > D)
+        return -1;
+    if (!(scale > 0.0))
+        scale = 1.0 / sqrt((double)D);
+    const int g = Hq / Hkv;
+    const int n_units = heads ? n_heads : B * Hq;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < n_units; u++) {
+        const int unit = heads ? heads[u] : u;
+        const int b = unit / Hq, h = unit % Hq;
+        const int kv = h / g;
+        const size_t base = ((size_t)b * Hkv + kv) * (size_t)S * D;
+        double *qr = (double *)malloc(sizeof(double) * (size_t)D);
+        double *w = (double *)malloc(sizeof(double) * (size_t)S);
+
+        /* the query in the PCA basis */
+        rotate_row(q, dtype, (size_t)unit * D, P + (size_t)kv * D * D, D, qr);
+
+        /* logits of every token from its leading d rotated coordinates */
+        double zmax = -INFINITY;
+        for (int t = 0; t < S; t++) {
+            double dot = 0.0;
+            for (int c = 0; c < d; c++)
+                dot += qr[c] * load_elem(krot, dtype, base + (size_t)t * D + c);
+            w[t] = scale * dot;
+            if (w[t] > zmax)
+                zmax = w[t];
+        }
+        /* softmax over all S tokens, then the weighted sum of the value rows */
+        double denom = 0.0;
+        for (int t = 0; t < S; t++) {
+            w[t] = exp(w[t] - zmax);
+            denom += w[t];
+        }
+        double *o = out + (size_t)unit * D;
+        for (int c = 0; c < D; c++) {
+            double acc = 0.0;
+            for (int t = 0; t < S; t++)
+                acc += w[t] * load_elem(v, dtype, base + (size_t)t * D + c);
+            o[c] = acc / denom;
+        }
+        free(qr);
+        free(w);
+    }
+    return 0;
+}
+
+/*
  * Append of one new token per (batch, KV head): the new key is rotated into
  * the PCA basis in fp64 and rounded once to the storage dtype; the value row
  * is stored unchanged.  (Poster page, "Loki's Computational Cost": the KV-cache

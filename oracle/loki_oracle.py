@@ -23,6 +23,11 @@ itself; see tests/test_oracle_pins.py):
                         convex-combination bounds; V outside idx irrelevant;
                         scaling V scales out; token permutation equivariance;
                         key centring invariance
+  pca_attention      -> d=D: textbook full attention on the unrotated keys and
+                        torch SDPA; any d: torch SDPA over the leading d
+                        rotated coordinates (P = identity: over the leading d
+                        raw coordinates) with the full-D softmax scale;
+                        convexity and V scaling
   append             -> fp64 projection equal to the prefilled rotation;
                         rounding equal to numpy float16 / torch bfloat16
   rounding           -> numpy float64->float16, torch float32->bfloat16 and
@@ -55,6 +60,8 @@ def lib():
         L.oracle_decode.restype = ip
         L.oracle_attend_given.argtypes = [ip] * 6 + [dp, ip] + [vp] * 5 + [vp, ip, vp]
         L.oracle_attend_given.restype = ip
+        L.oracle_pca_attention.argtypes = [ip] * 6 + [dp, ip] + [vp] * 4 + [vp, ip, vp]
+        L.oracle_pca_attention.restype = ip
         L.oracle_append_rows.argtypes = [ip] * 4 + [vp] * 5
         L.oracle_append_rows.restype = ip
         L.oracle_rotate_queries.argtypes = [ip] * 5 + [vp] * 3
@@ -137,6 +144,26 @@ def attend_given(q, krot, v, P, idx, dtype, scale=0.0, heads=None):
                                    _ptr(hh), nh, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_attend_given: bad arguments or index out of range")
+    return out
+
+
+def pca_attention(q, krot, v, P, d, dtype, scale=0.0, heads=None):
+    """PCAAttn in fp64: softmax over all S tokens of scale * (low-dim score),
+    weighted sum of all S value rows.  Shapes as decode; returns out [B,Hq,D]."""
+    q = _check_storage(q, dtype)
+    krot = _check_storage(krot, dtype)
+    v = _check_storage(v, dtype)
+    B, Hq, D = q.shape
+    _, Hkv, S, D2 = krot.shape
+    assert D2 == D and v.shape == krot.shape and P.shape == (Hkv, D, D)
+    P64 = _c(P, np.float64)
+    out = np.zeros((B, Hq, D), np.float64)
+    hh, nh = _heads(heads)
+    rc = lib().oracle_pca_attention(B, Hq, Hkv, S, D, int(d), float(scale), DTYPE_CODE[dtype],
+                                    _ptr(q), _ptr(krot), _ptr(v), _ptr(P64), _ptr(hh), nh,
+                                    _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_pca_attention: argument outside the method's domain")
     return out
 
 

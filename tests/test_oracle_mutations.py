@@ -29,6 +29,10 @@ MUTANTS = [
      "for (int j = 0; j < D / 2; j++)\n            acc += qr[j] * load_elem(krot"),
     ("half_round_down", "if (frac > 0.5 || (frac == 0.5 && fmod(f, 2.0) != 0.0))",
      "if (frac > 0.5)"),
+    ("pca_no_scale", "w[t] = scale * dot;", "w[t] = dot;"),
+    ("pca_all_coordinates", "for (int c = 0; c < d; c++)\n                dot +=",
+     "for (int c = 0; c < D; c++)\n                dot +="),
+    ("pca_mean_instead_of_softmax", "o[c] = acc / denom;", "o[c] = acc / S;"),
     ("bf16_bias_off", "return sign | (uint16_t)encode_small_float(fabs(v), 7, -126, 127, ovf, 0x7f80);",
      "return sign | (uint16_t)encode_small_float(fabs(v), 7, -126, 126, ovf, 0x7f80);"),
 ]

@@ -279,6 +279,56 @@ def test_structure_convexity_support_scaling(oracle):
     assert np.array_equal(r3["out"], r["out"] * 4.0)
 
 
+# ------------------------------------------------------------- PCAAttn pins
+
+def _sdpa(q, K, V, scale):
+    """torch scaled_dot_product_attention (CPU fp64), one query row per (b, h)."""
+    B, Hq, _ = q.shape
+    g = Hq // K.shape[1]
+    Kq = torch.from_numpy(np.ascontiguousarray(np.repeat(K, g, axis=1)))
+    Vq = torch.from_numpy(np.ascontiguousarray(np.repeat(V, g, axis=1)))
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(q))[:, :, None, :], Kq, Vq,
+        scale=scale)[:, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2)])
+def test_pca_attention_full_d_is_full_attention(oracle, Hq, Hkv):
+    q, K, krot, V, P = _case(B=2, Hq=Hq, Hkv=Hkv, S=45, D=16, seed=90 + Hq)
+    out = oracle.pca_attention(q, krot, V, P, 16, "f64")
+    np.testing.assert_allclose(out, _full_attention(q, K, V), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("d", [1, 4, 11])
+def test_pca_attention_is_attention_over_leading_coordinates(oracle, d):
+    """Any d: SDPA over the leading d rotated coordinates of query and keys, with
+    the full-dimension scale; with P = identity, over the leading d raw ones."""
+    q, K, krot, V, P = _case(B=2, Hq=4, Hkv=2, S=60, D=16, seed=95 + d)
+    D = 16
+    qr = np.einsum("bhi,hij->bhj", q, np.repeat(P, 2, axis=0))
+    out = oracle.pca_attention(q, krot, V, P, d, "f64")
+    ref = _sdpa(qr[..., :d], krot[..., :d], V, 1.0 / math.sqrt(D))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    eye = np.broadcast_to(np.eye(D), P.shape).copy()
+    out_i = oracle.pca_attention(q, K, V, eye, d, "f64")
+    np.testing.assert_allclose(out_i, _sdpa(q[..., :d], K[..., :d], V, 1.0 / math.sqrt(D)),
+                               rtol=0, atol=1e-12)
+    # a given scale replaces 1/sqrt(D)
+    out_s = oracle.pca_attention(q, krot, V, P, d, "f64", scale=0.7)
+    np.testing.assert_allclose(out_s, _sdpa(qr[..., :d], krot[..., :d], V, 0.7), rtol=0,
+                               atol=1e-12)
+
+
+def test_pca_attention_structure(oracle):
+    q, K, krot, V, P = _case(S=50, D=16, seed=99)
+    out = oracle.pca_attention(q, krot, V, P, 5, "f64")
+    assert np.all(out >= V.min(axis=2) - 1e-15) and np.all(out <= V.max(axis=2) + 1e-15)
+    np.testing.assert_array_equal(oracle.pca_attention(q, krot, V * 2.0, P, 5, "f64"), out * 2.0)
+    q0 = np.zeros_like(q)
+    np.testing.assert_allclose(oracle.pca_attention(q0, krot, V, P, 5, "f64"), V.mean(axis=2),
+                               rtol=0, atol=1e-15)
+
+
 def test_token_permutation_equivariance(oracle):
     q, K, krot, V, P = _case(B=1, Hq=1, Hkv=1, S=70, D=16, seed=63)
     perm = np.random.default_rng(64).permutation(70)
