@@ -237,6 +237,14 @@ def main():
                                                       out_, cd, wsf_, ws_full.numel(), st))
     es_ = 4 if wl.dtype == "f32" else 2
     full_bytes = es_ * wl.B * wl.Hkv * wl.S * wl.D * 2
+    # PCAAttn, the pages' variant attending with the d-dim scores over all S
+    chk(lib.loki_pca_attention(q_, kcs[0], vcs[0], P_, wl.d, out_, cd, wsf_, ws_full.numel(), st))
+    pca_us = timed(lambda i: lib.loki_pca_attention(q_, kcs[i % len(kcs)], vcs[i % len(vcs)], P_,
+                                                    wl.d, out_, cd, wsf_, ws_full.numel(), st))
+    pca_bytes = es_ * wl.B * wl.Hkv * wl.S * (wl.d + wl.D)
+    pca = {"us_per_step": round(pca_us, 2), "kv_bytes_per_step": pca_bytes,
+           "GBps": round(pca_bytes / (pca_us * 1e-6) / 1e9, 1),
+           "loki_speedup": round(pca_us / (ms_per_step * 1e3), 3)}
     del ws_full
 
     # Exact-TopK, the pages' other baseline: scores over all D coordinates
@@ -321,6 +329,7 @@ def main():
                            "GBps": round(full_bytes / (full_us * 1e-6) / 1e9, 1),
                            "loki_speedup": round(full_us / (ms_per_step * 1e3), 3)},
         "exact_topk": exact,
+        "pca_attention": pca,
         "prefill": prefill,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -19,7 +19,11 @@
  *   [C]  same page, "In-depth insights", "Loki's Computational Cost": the
  *        KV-cache append is part of each step;
  *   [TB] same page, "More on tables", first table: k_f is the fraction of keys
- *        kept, d_f the fraction of the key dimensions used for scoring.
+ *        kept, d_f the fraction of the key dimensions used for scoring;
+ *   [S]  same page, "More on figures": per-layer attention time of vanilla
+ *        attention against Loki (Llama2-13B), the speed-up being measured;
+ *   [PT] same page, "More on tables", the PCAAttn table: a Loki variant that
+ *        attends with the reduced-dimensional scores directly.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, at least
@@ -226,6 +230,19 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
 int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
                         float* out, const loki_desc* desc, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * PCAAttn [PT]: the Loki variant that attends with the reduced-dimensional
+ * scores directly.  qr = q . P[kv], z_t = scale * sum_{j<d} qr_j krot_{t,j}
+ * for every token t < S (no selection), out = softmax(z) . V over all S
+ * tokens.  1 <= d <= D; d = D gives loki_full_attention's result.  Reads the
+ * leading d coordinates of each cached key (the panel when d <= panel_dim)
+ * and every V row.  out [B, Hq, D] fp32.  Needs
+ * loki_workspace_bytes(desc, D, seq_len) bytes of workspace.
+ */
+int loki_pca_attention(const void* q, const void* kcache, const void* vcache, const float* P,
+                       int d, float* out, const loki_desc* desc, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ STATUS = {0: "LOKI_OK", -1: "LOKI_EINVAL", -2: "LOKI_EUNSUPPORTED", -3: "LOKI_EW
 EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_workspace_bytes",
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
-           "loki_decode_plan", "loki_full_attention", "loki_prefill"]
+           "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention"]
 
 
 class _CDesc(ctypes.Structure):
@@ -69,6 +69,7 @@ _SIG = {
                            _i),
     "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
     "loki_full_attention": ([_vp, _vp, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
+    "loki_pca_attention": ([_vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
     "loki_prefill": ([_vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _D, _vp], _i),
 }
 for _name, (_args, _res) in _SIG.items():
@@ -308,6 +309,23 @@ def full_attention(q, kcache, vcache, P, desc: Desc, out=None, workspace=None, s
     _check(_lib.loki_full_attention(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), _ptr(out),
                                     ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "loki_full_attention")
+    return out
+
+
+def pca_attention(q, kcache, vcache, P, d: int, desc: Desc, out=None, workspace=None,
+                  stream=None):
+    """PCAAttn: softmax over all seq_len tokens of the scaled scores from the
+    leading d rotated coordinates, weighted sum of all V rows; returns out
+    [B, Hq, D] fp32."""
+    _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    if workspace is None:
+        workspace = empty_workspace(desc, desc.head_dim, desc.seq_len, q.device)
+    _check(_lib.loki_pca_attention(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), d, _ptr(out),
+                                   ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)), "loki_pca_attention")
     return out
 
 

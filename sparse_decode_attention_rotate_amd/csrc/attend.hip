@@ -12,6 +12,9 @@
 // Without an index list (idx == null) row r is token r: dense decode
 // attention over all S cached tokens, the full-attention baseline the pages
 // compare Loki with (poster page "TL;DR": speed-up over vanilla attention).
+// With low_dim set as well the logits use only the leading d rotated
+// coordinates: PCAAttn, the Loki variant that attends with the
+// reduced-dimensional scores directly (poster page, "More on tables").
 #include "attend_core.h"
 #include "loki_internal.h"
 
@@ -21,7 +24,7 @@ namespace {
 
 constexpr int kAttThreads = 256;
 
-template <int DT, int D, bool SPLIT>
+template <int DT, int D, bool SPLIT, bool LOW>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __shared__ int sidx[kAttendChunk];
   __shared__ float slow[kAttendChunk];
@@ -45,8 +48,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __syncthreads();
 
   float M, L, A;
-  block_attend<DT, D, kAttThreads, SPLIT>(p.qr + bh * D, p.scale_log2, sidx, slow, nr, p.kcache,
-                                          p.vcache, head, sh, sm, M, L, A);
+  block_attend<DT, D, kAttThreads, SPLIT, kRowsPerBatch, LOW>(
+      p.qr + bh * D, p.scale_log2, sidx, slow, nr, p.kcache, p.vcache, head, sh, sm, M, L, A, p.d);
   if (tid < D) {
     if (p.nsplit == 1) {
       p.out[bh * D + tid] = A / L;
@@ -81,9 +84,11 @@ template <int DT, int D>
 hipError_t launch_d(const AttendParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.nsplit * p.sh.B * p.sh.Hq));
   if (p.sel_scores)
-    attend_kernel<DT, D, true><<<grid, kAttThreads, 0, st>>>(p);
+    attend_kernel<DT, D, true, false><<<grid, kAttThreads, 0, st>>>(p);
+  else if (p.low_dim)
+    attend_kernel<DT, D, false, true><<<grid, kAttThreads, 0, st>>>(p);
   else
-    attend_kernel<DT, D, false><<<grid, kAttThreads, 0, st>>>(p);
+    attend_kernel<DT, D, false, false><<<grid, kAttThreads, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   combine_kernel<D><<<dim3((unsigned)(p.sh.B * p.sh.Hq)), D, 0, st>>>(p);

@@ -16,6 +16,10 @@
 // Split variant (the leading dp coordinates were already multiplied during
 // scoring and their partial logits are given): only the remaining D-dp key
 // coordinates are read, z_t = scale * (s_low_t + sum_{j>=dp} qr_j krot_{t,j}).
+//
+// Low-dimensional variant (LOW, PCAAttn): the logits use only the leading
+// kdim rotated coordinates, z_t = scale * sum_{j<kdim} qr_j krot_{t,j}; key
+// chunks wholly past kdim are not read.
 #pragma once
 
 #include "loki_internal.h"
@@ -45,13 +49,13 @@ struct AttendSmem {
 // head: flattened (b, kv) of the caches.  On return thread tid < D holds the
 // merged (M, L, A) with A the unnormalised output coordinate tid, in the log2
 // domain: out[tid] = A / L.
-template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch>
+template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch, bool LOW = false>
 __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2,
                                              const int* sidx, const float* slow, int nr,
                                              const void* kcache, const void* vcache,
                                              size_t head, const Shape& sh,
                                              AttendSmem<DT, D, NT>& sm, float& M_out,
-                                             float& L_out, float& A_out) {
+                                             float& L_out, float& A_out, int kdim = D) {
   using G = AttendGeom<DT, D, NT>;
   constexpr int EB = G::EB, E = G::E, LPR = G::LPR, RPI = G::RPI, NG = G::NG;
   constexpr int ROWS_PER_ITER = 2 * RB * NG;  // two batches in flight
@@ -68,10 +72,10 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
   for (int e = 0; e < E; e++) {
     const int j = j0 + e;
     const float v = qrow[j] * scale_log2;
-    qv[e] = (SPLIT && j < sh.dp) ? 0.f : v;
+    qv[e] = ((SPLIT && j < sh.dp) || (LOW && j >= kdim)) ? 0.f : v;
   }
   // byte offset of this lane's key chunk inside a row's part of the cache
-  const bool k_needed = !SPLIT || j0 >= sh.dp;
+  const bool k_needed = (!SPLIT || j0 >= sh.dp) && (!LOW || j0 < kdim);
   const bool in_panel = j0 < sh.dp;
   const uint32_t k_row_bytes = (uint32_t)((in_panel ? sh.dp : sh.kl.rest) * EB);
   const uint32_t k_base = (uint32_t)((in_panel ? (size_t)j0 : sh.kl.rest_off + (j0 - sh.dp)) * EB);

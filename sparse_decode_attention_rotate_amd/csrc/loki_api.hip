@@ -510,9 +510,12 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
                      workspace_bytes, stream, true);
 }
 
-int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
-                        float* out, const loki_desc* desc, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+// Dense (low_dim = 0) or low-dimensional (PCAAttn) attention over all S
+// tokens: query rotation, then the split attention with identity rows.
+static int all_tokens_attention(const void* q, const void* kcache, const void* vcache,
+                                const float* P, int d, int low_dim, float* out,
+                                const loki_desc* desc, void* workspace, size_t workspace_bytes,
+                                void* stream, const char* what) {
   Shape sh;
   int rc = check_desc(desc, &sh);
   if (rc) return rc;
@@ -522,6 +525,7 @@ int loki_full_attention(const void* q, const void* kcache, const void* vcache, c
   REQUIRE_PTR(P);
   REQUIRE_PTR(out);
   REQUIRE_PTR(workspace);
+  if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "%s: d = %d outside [1, %d]", what, d, sh.D);
   const WsLayout w = ws_layout(sh, sh.S);
   if (workspace_bytes < w.total)
     return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, w.total);
@@ -547,12 +551,28 @@ int loki_full_attention(const void* q, const void* kcache, const void* vcache, c
   ap.out = out;
   ap.part = reinterpret_cast<float*>(ws + w.part);
   ap.k = sh.S;
-  ap.d = sh.D;
+  ap.d = d;
+  ap.low_dim = low_dim;
   ap.nsplit = w.nsplit;
   ap.kc = kAttendChunk;
   ap.scale_log2 = scale_log2(desc);
   ap.sh = sh;
-  return hip_status(launch_attend(ap, st), "attend");
+  return hip_status(launch_attend(ap, st), what);
+}
+
+int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
+                        float* out, const loki_desc* desc, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int D = desc ? desc->head_dim : 1;
+  return all_tokens_attention(q, kcache, vcache, P, D, 0, out, desc, workspace, workspace_bytes,
+                              stream, "full_attention");
+}
+
+int loki_pca_attention(const void* q, const void* kcache, const void* vcache, const float* P,
+                       int d, float* out, const loki_desc* desc, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return all_tokens_attention(q, kcache, vcache, P, d, 1, out, desc, workspace, workspace_bytes,
+                              stream, "pca_attention");
 }
 
 }  // extern "C"

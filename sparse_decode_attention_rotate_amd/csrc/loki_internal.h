@@ -54,6 +54,7 @@ struct AttendParams {
   float* out;               // [B,Hq,D] fp32 (written when nsplit == 1 or by combine)
   float* part;              // [B*Hq, nsplit, D+2] partial (m, l, acc)
   int k, d, nsplit, kc;
+  int low_dim;              // logits from the leading d coordinates only (PCAAttn)
   float scale_log2;         // softmax scale * log2(e)
   Shape sh;
 };

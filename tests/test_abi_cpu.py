@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for n in ["loki_decode", "loki_decode_append", "loki_append", "loki_rotate_query",
               "loki_score", "loki_topk", "loki_attend", "loki_pack_kcache", "loki_unpack_kcache",
               "loki_workspace_bytes", "loki_kcache_elems", "loki_strerror", "loki_last_error",
-              "loki_decode_plan", "loki_full_attention", "loki_prefill"]:
+              "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention"]:
         assert n in names
 
 
@@ -137,6 +137,12 @@ def test_other_entry_points_validate(L):
     assert fa(odd, fake, fake, fake, fake, cd, fake, 1 << 30, None) == -1   # misaligned q
     assert fa(fake, fake, fake, fake, fake, None, fake, 1 << 30, None) == -1  # desc NULL
     assert fa(fake, fake, fake, fake, fake, cd, fake, 16, None) == -3       # workspace
+    pa = lib.loki_pca_attention
+    assert pa(fake, fake, fake, fake, 0, fake, cd, fake, 1 << 30, None) == -1    # d = 0
+    assert pa(fake, fake, fake, fake, 129, fake, cd, fake, 1 << 30, None) == -1  # d > D
+    assert pa(fake, fake, fake, fake, 32, None, cd, fake, 1 << 30, None) == -1   # out NULL
+    assert pa(fake, fake, fake, fake, 32, fake, cd, fake, 16, None) == -3        # workspace
+    assert pa(fake, fake, fake, fake, 32, fake, None, fake, 1 << 30, None) == -1  # desc NULL
     pf = lib.loki_prefill
     assert pf(fake, None, 129, 0, fake, fake, None, cd, None) == -1     # past S_cap
     assert pf(fake, None, 100, 29, fake, fake, None, cd, None) == -1    # pos + n past S_cap

@@ -545,6 +545,45 @@ def test_full_attention(L, dtype, Hq, Hkv, S):
     assert H.rel_err_rows(out, ref).max() < H.OUT_TOL[dtype]
 
 
+# ----------------------------------------------------------------- PCAAttn
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,S,d,dp,D", [
+    ("f16", 4, 4, 3000, 32, 32, 128), ("bf16", 8, 2, 2600, 20, 32, 128),
+    ("f32", 2, 2, 1500, 48, 32, 128), ("f16", 4, 2, 700, 128, 32, 128),
+    ("bf16", 2, 2, 513, 7, 16, 128), ("f16", 4, 4, 1100, 16, 16, 64)])
+def test_pca_attention(L, dtype, Hq, Hkv, S, d, dp, D):
+    """PCAAttn: softmax over all tokens of the scaled low-dimensional scores."""
+    wl = _small(dtype, Hq=Hq, Hkv=Hkv, S=S, D=D, k=min(S, 300), d=min(d, 32))
+    H.log(f"pca attention {dtype} Hq={Hq} Hkv={Hkv} S={S} d={d} dp={dp} D={D}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x, dp)
+    out = L.pca_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], d, dev["desc"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    ref = oracle.pca_attention(x["q"], x["krot"], x["v"], x["P"], d, dtype)
+    err = H.rel_err_rows(out, ref)
+    H.log(f"  max rel err {err.max():.3e}")
+    assert np.all(np.isfinite(out))
+    assert err.max() < H.OUT_TOL[dtype]
+
+
+def test_pca_attention_full_size(L):
+    """Llama2-13B shape (the launch the bench times), sampled query heads."""
+    wl = W.get("llama2_13b_f16")
+    H.log("pca attention full size llama2_13b_f16")
+    x = W.generate(wl)
+    dev = H.upload(wl, x, wl.d)
+    out = L.pca_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, dev["desc"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    heads = np.random.default_rng(5).choice(wl.B * wl.Hq, 48, replace=False)
+    ref = oracle.pca_attention(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.dtype, heads=heads)
+    for u in heads:
+        b, h = divmod(int(u), wl.Hq)
+        assert H.rel_err_rows(out[b, h][None], ref[b, h][None]).max() < H.OUT_TOL[wl.dtype]
+    assert np.all(np.isfinite(out))
+
+
 # ------------------------------------------------------------- Exact-TopK
 
 @pytest.mark.parametrize("dtype,g", [("f16", 1), ("bf16", 4)])
