@@ -469,6 +469,45 @@ int oracle_pca_attention(int B, int Hq, int Hkv, int S, int D, int d, double sca
 }
 
 /*
+ * Calibration covariance (poster page, "Visual Insights", Figure 1 right, and
+ * "More on figures": principal component analysis of the keys of a
+ * calibration set, done offline).  For each KV head, with the n calibration
+ * keys x_t (storage dtype, [Hkv, n, D]): mu = (1/n) sum_t x_t and
+ * C = (1/n) sum_t (x_t - mu)(x_t - mu)^T, in fp64.  cov [Hkv, D, D].
+ */
+int oracle_covariance(int Hkv, int n, int D, int dtype, const void *keys, double *cov)
+{
+    if (Hkv < 1 || n < 1 || D < 1)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int kv = 0; kv < Hkv; kv++) {
+        const size_t kbase = (size_t)kv * n * D;
+        double *mean = (double *)calloc((size_t)D, sizeof(double));
+        double *xc = (double *)malloc(sizeof(double) * (size_t)D);
+        double *C = cov + (size_t)kv * D * D;
+        for (int t = 0; t < n; t++)
+            for (int i = 0; i < D; i++)
+                mean[i] += load_elem(keys, dtype, kbase + (size_t)t * D + i);
+        for (int i = 0; i < D; i++)
+            mean[i] /= (double)n;
+        for (size_t e = 0; e < (size_t)D * D; e++)
+            C[e] = 0.0;
+        for (int t = 0; t < n; t++) {
+            for (int i = 0; i < D; i++)
+                xc[i] = load_elem(keys, dtype, kbase + (size_t)t * D + i) - mean[i];
+            for (int i = 0; i < D; i++)
+                for (int jj = 0; jj < D; jj++)
+                    C[(size_t)i * D + jj] += xc[i] * xc[jj];
+        }
+        for (size_t e = 0; e < (size_t)D * D; e++)
+            C[e] /= (double)n;
+        free(mean);
+        free(xc);
+    }
+    return 0;
+}
+
+/*
  * Append of one new token per (batch, KV head): the new key is rotated into
  * the PCA basis in fp64 and rounded once to the storage dtype; the value row
  * is stored unchanged.  (Poster page, "Loki's Computational Cost": the KV-cache

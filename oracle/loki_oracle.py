@@ -28,6 +28,10 @@ itself; see tests/test_oracle_pins.py):
                         rotated coordinates (P = identity: over the leading d
                         raw coordinates) with the full-D softmax scale;
                         convexity and V scaling
+  covariance         -> numpy.cov(bias=True); keys built from Hadamard columns
+                        with an exactly known covariance Q diag(sigma^2) Q^T
+  calibrate          -> that closed form (P = Q with the sign rule, variances
+                        sigma^2); eigen-residual, orthonormality, order, signs
   append             -> fp64 projection equal to the prefilled rotation;
                         rounding equal to numpy float16 / torch bfloat16
   rounding           -> numpy float64->float16, torch float32->bfloat16 and
@@ -62,6 +66,8 @@ def lib():
         L.oracle_attend_given.restype = ip
         L.oracle_pca_attention.argtypes = [ip] * 6 + [dp, ip] + [vp] * 4 + [vp, ip, vp]
         L.oracle_pca_attention.restype = ip
+        L.oracle_covariance.argtypes = [ip] * 4 + [vp, vp]
+        L.oracle_covariance.restype = ip
         L.oracle_append_rows.argtypes = [ip] * 4 + [vp] * 5
         L.oracle_append_rows.restype = ip
         L.oracle_rotate_queries.argtypes = [ip] * 5 + [vp] * 3
@@ -165,6 +171,36 @@ def pca_attention(q, krot, v, P, d, dtype, scale=0.0, heads=None):
     if rc != 0:
         raise ValueError("oracle_pca_attention: argument outside the method's domain")
     return out
+
+
+def covariance(keys, dtype):
+    """Centred (1/n) covariance [Hkv, D, D] fp64 of calibration keys [Hkv, n, D]."""
+    keys = _check_storage(keys, dtype)
+    Hkv, n, D = keys.shape
+    cov = np.zeros((Hkv, D, D), np.float64)
+    if lib().oracle_covariance(Hkv, n, D, DTYPE_CODE[dtype], _ptr(keys), _ptr(cov)) != 0:
+        raise ValueError("oracle_covariance: bad arguments")
+    return cov
+
+
+def calibrate(keys, dtype):
+    """PCA of calibration keys [Hkv, n, D] (poster page, "Visual Insights",
+    Figure 1 right): per KV head the eigenvectors of the centred covariance as
+    the columns of P, variances descending (equal ones keep their eigh order),
+    each column's largest-magnitude entry (the first such) made positive.
+    Returns (P [Hkv, D, D] fp64, variances [Hkv, D] fp64)."""
+    cov = covariance(keys, dtype)
+    Hkv, D, _ = cov.shape
+    P = np.zeros((Hkv, D, D))
+    var = np.zeros((Hkv, D))
+    for kv in range(Hkv):
+        w, V = np.linalg.eigh(cov[kv])
+        order = np.argsort(-w, kind="stable")
+        w, V = w[order], V[:, order]
+        lead = np.argmax(np.abs(V), axis=0)
+        V = V * np.where(V[lead, np.arange(D)] < 0, -1.0, 1.0)
+        P[kv], var[kv] = V, w
+    return P, var
 
 
 def append_rows(k_new, v_new, P, dtype):

@@ -33,6 +33,9 @@ MUTANTS = [
     ("pca_all_coordinates", "for (int c = 0; c < d; c++)\n                dot +=",
      "for (int c = 0; c < D; c++)\n                dot +="),
     ("pca_mean_instead_of_softmax", "o[c] = acc / denom;", "o[c] = acc / S;"),
+    ("cov_not_centred", "xc[i] = load_elem(keys, dtype, kbase + (size_t)t * D + i) - mean[i];",
+     "xc[i] = load_elem(keys, dtype, kbase + (size_t)t * D + i);"),
+    ("cov_n_minus_1", "C[e] /= (double)n;", "C[e] /= (double)(n - 1);"),
     ("bf16_bias_off", "return sign | (uint16_t)encode_small_float(fabs(v), 7, -126, 127, ovf, 0x7f80);",
      "return sign | (uint16_t)encode_small_float(fabs(v), 7, -126, 126, ovf, 0x7f80);"),
 ]

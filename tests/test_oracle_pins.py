@@ -329,6 +329,52 @@ def test_pca_attention_structure(oracle):
                                rtol=0, atol=1e-15)
 
 
+# --------------------------------------------------------- calibration pins
+
+def test_covariance_matches_numpy_cov(oracle):
+    g = np.random.default_rng(120)
+    keys = g.standard_normal((3, 200, 16)) * np.linspace(2.0, 0.1, 16) + 5.0
+    C = oracle.covariance(keys, "f64")
+    for kv in range(3):
+        np.testing.assert_allclose(C[kv], np.cov(keys[kv].T, bias=True), rtol=0, atol=1e-12)
+    k16 = keys.astype(np.float16)
+    C16 = oracle.covariance(k16, "f16")
+    np.testing.assert_allclose(C16[1], np.cov(k16[1].astype(np.float64).T, bias=True), rtol=0,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("D", [16, 128])
+def test_calibrate_closed_form_hadamard(oracle, D):
+    """Keys x_t = Z[t] diag(sigma) Q^T + mu with Z = columns 1..D of a 256 x 256
+    Hadamard matrix (entries +-1, zero column sums, Z^T Z = 256 I): the centred
+    covariance is exactly Q diag(sigma^2) Q^T, so P = Q (sign rule applied) and
+    the variances are sigma^2, whatever the offset mu."""
+    from scipy.linalg import hadamard
+    Z = hadamard(256).astype(np.float64)[:, 1:D + 1]
+    Q = _orthonormal(D, 121 + D)
+    sig = np.linspace(3.0, 0.5, D)
+    mu = np.random.default_rng(122).standard_normal(D) * 4.0
+    keys = (Z * sig) @ Q.T + mu
+    P, var = oracle.calibrate(keys[None], "f64")
+    np.testing.assert_allclose(var[0], sig ** 2, rtol=0, atol=1e-11)
+    lead = np.argmax(np.abs(Q), axis=0)
+    Qs = Q * np.sign(Q[lead, np.arange(D)])
+    np.testing.assert_allclose(P[0], Qs, rtol=0, atol=1e-9)
+
+
+def test_calibrate_eigen_properties(oracle):
+    g = np.random.default_rng(123)
+    keys = g.standard_normal((2, 500, 32)) * np.exp(-np.arange(32) / 8.0)
+    P, var = oracle.calibrate(keys, "f64")
+    C = oracle.covariance(keys, "f64")
+    for kv in range(2):
+        np.testing.assert_allclose(C[kv] @ P[kv], P[kv] * var[kv], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(P[kv].T @ P[kv], np.eye(32), rtol=0, atol=1e-12)
+        assert np.all(np.diff(var[kv]) <= 0)
+        lead = np.argmax(np.abs(P[kv]), axis=0)
+        assert np.all(P[kv][lead, np.arange(32)] > 0)
+
+
 def test_token_permutation_equivariance(oracle):
     q, K, krot, V, P = _case(B=1, Hq=1, Hkv=1, S=70, D=16, seed=63)
     perm = np.random.default_rng(64).permutation(70)
