@@ -286,7 +286,23 @@ def main():
                "frac_hbm_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                "copy_same_bytes_us": round(copy_us, 2),
                "frac_of_copy_rate": round(copy_us / prefill_us, 4)}
-    del k_rows, kc_p, cp_dst
+    # calibration: PCA of n_calib keys per KV head on the GPU (offline step)
+    keys_cal = k_rows[0, :, :wl.n_calib].contiguous()
+    P_cal = torch.empty_like(P)
+    var_cal = torch.empty((wl.Hkv, wl.D), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t()
+    chk(lib.loki_calibrate_workspace_bytes(cd, wl.n_calib, ctypes.byref(nb)))
+    ws_cal = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    cal_args = (vp(keys_cal.data_ptr()), wl.n_calib, vp(P_cal.data_ptr()), vp(var_cal.data_ptr()),
+                cd, vp(ws_cal.data_ptr()), ws_cal.numel(), st)
+    chk(lib.loki_calibrate(*cal_args))
+    saved_steps, args.steps = args.steps, min(args.steps, 20)
+    cal_us = timed(lambda i: lib.loki_calibrate(*cal_args))
+    args.steps = saved_steps
+    calibration = {"us_per_call": round(cal_us, 1), "keys_per_head": wl.n_calib,
+                   "kv_heads": wl.Hkv,
+                   "covariance_GFLOP": round(2.0 * wl.Hkv * wl.n_calib * wl.D * wl.D / 1e9, 3)}
+    del k_rows, kc_p, cp_dst, keys_cal, ws_cal
 
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()
@@ -331,6 +347,7 @@ def main():
         "exact_topk": exact,
         "pca_attention": pca,
         "prefill": prefill,
+        "calibration": calibration,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

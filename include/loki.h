@@ -23,7 +23,9 @@
  *   [S]  same page, "More on figures": per-layer attention time of vanilla
  *        attention against Loki (Llama2-13B), the speed-up being measured;
  *   [PT] same page, "More on tables", the PCAAttn table: a Loki variant that
- *        attends with the reduced-dimensional scores directly.
+ *        attends with the reduced-dimensional scores directly;
+ *   [FG] same page, "More on figures": the rank at which PCA of the keys
+ *        explains 90% of their variance, and the offline PCA calibration step.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, at least
@@ -243,6 +245,24 @@ int loki_full_attention(const void* q, const void* kcache, const void* vcache, c
 int loki_pca_attention(const void* q, const void* kcache, const void* vcache, const float* P,
                        int d, float* out, const loki_desc* desc, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Calibration [F1], [FG]: the offline PCA that yields P, run on the GPU.
+ * keys [Hkv, n, D] in the storage dtype: n >= 1 unrotated calibration keys
+ * per KV head (only n_kv_heads, head_dim and dtype of desc are used, the rest
+ * must still be valid).  Per KV head: C = (1/n) sum_t (x_t - mu)(x_t - mu)^T,
+ * its eigenvectors written as the columns of P [Hkv, D, D] (fp32, row-major,
+ * the layout every other call takes), ordered by descending eigenvalue, each
+ * signed so that its first largest-magnitude entry is positive; variances
+ * (nullable, [Hkv, D] fp32) receives the eigenvalues in the same order.
+ * Accuracy: covariance from exact three-part bf16 products accumulated in
+ * fp32, eigenvectors by fp32 Jacobi rotations; an eigenvector whose
+ * eigenvalue is close to another's is determined only as far as that gap
+ * allows.  Needs loki_calibrate_workspace_bytes(desc, n) bytes of workspace.
+ */
+int loki_calibrate_workspace_bytes(const loki_desc* desc, int32_t n, size_t* bytes);
+int loki_calibrate(const void* keys, int32_t n, float* P, float* variances,
+                   const loki_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

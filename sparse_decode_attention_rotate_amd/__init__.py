@@ -39,7 +39,8 @@ STATUS = {0: "LOKI_OK", -1: "LOKI_EINVAL", -2: "LOKI_EUNSUPPORTED", -3: "LOKI_EW
 EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_workspace_bytes",
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
-           "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention"]
+           "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention",
+           "loki_calibrate_workspace_bytes", "loki_calibrate"]
 
 
 class _CDesc(ctypes.Structure):
@@ -70,6 +71,8 @@ _SIG = {
     "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
     "loki_full_attention": ([_vp, _vp, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
     "loki_pca_attention": ([_vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
+    "loki_calibrate_workspace_bytes": ([_D, ctypes.c_int32, ctypes.POINTER(_sz)], _i),
+    "loki_calibrate": ([_vp, ctypes.c_int32, _vp, _vp, _D, _vp, _sz, _vp], _i),
     "loki_prefill": ([_vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _D, _vp], _i),
 }
 for _name, (_args, _res) in _SIG.items():
@@ -327,6 +330,27 @@ def pca_attention(q, kcache, vcache, P, d: int, desc: Desc, out=None, workspace=
                                    ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
                                    _stream(stream)), "loki_pca_attention")
     return out
+
+
+def calibrate(keys, desc: Desc, P=None, variances=None, workspace=None, stream=None):
+    """PCA of calibration keys [Hkv, n, D] (storage dtype) on the GPU; returns
+    (P [Hkv, D, D] fp32, variances [Hkv, D] fp32)."""
+    Hkv, D = desc.n_kv_heads, desc.head_dim
+    n = keys.shape[1] if keys.dim() == 3 else -1
+    _expect(keys, (Hkv, n, D), desc.torch_dtype, "keys")
+    if P is None:
+        P = torch.empty((Hkv, D, D), dtype=torch.float32, device=keys.device)
+    if variances is None:
+        variances = torch.empty((Hkv, D), dtype=torch.float32, device=keys.device)
+    if workspace is None:
+        nb = ctypes.c_size_t()
+        _check(_lib.loki_calibrate_workspace_bytes(ctypes.byref(desc.c()), n, ctypes.byref(nb)),
+               "loki_calibrate_workspace_bytes")
+        workspace = torch.empty(nb.value, dtype=torch.uint8, device=keys.device)
+    _check(_lib.loki_calibrate(_ptr(keys), n, _ptr(P), _ptr(variances), ctypes.byref(desc.c()),
+                               _ptr(workspace), workspace.numel(), _stream(stream)),
+           "loki_calibrate")
+    return P, variances
 
 
 def strerror(code: int) -> str:

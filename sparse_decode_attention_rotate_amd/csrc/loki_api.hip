@@ -575,4 +575,46 @@ int loki_pca_attention(const void* q, const void* kcache, const void* vcache, co
                               stream, "pca_attention");
 }
 
+static size_t calib_part_bytes(const Shape& sh, int n, int* nch) {
+  *nch = (n + kCalChunk - 1) / kCalChunk;
+  return align256((size_t)sh.Hkv * *nch * sh.D * sh.D * 4);
+}
+
+int loki_calibrate_workspace_bytes(const loki_desc* desc, int32_t n, size_t* bytes) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  if (!bytes) return fail(LOKI_EINVAL, "bytes is NULL");
+  if (n < 1) return fail(LOKI_EINVAL, "n = %d calibration keys (need >= 1)", n);
+  int nch = 0;
+  *bytes = calib_part_bytes(sh, n, &nch) + align256((size_t)sh.Hkv * nch * sh.D * 4);
+  return LOKI_OK;
+}
+
+int loki_calibrate(const void* keys, int32_t n, float* P, float* variances,
+                   const loki_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape sh;
+  int rc = check_desc(desc, &sh);
+  if (rc) return rc;
+  REQUIRE_PTR(keys);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(workspace);
+  if (variances && !aligned16(variances)) return fail(LOKI_EINVAL, "variances is not 16-byte aligned");
+  if (n < 1) return fail(LOKI_EINVAL, "n = %d calibration keys (need >= 1)", n);
+  size_t need = 0;
+  if ((rc = loki_calibrate_workspace_bytes(desc, n, &need))) return rc;
+  if (workspace_bytes < need)
+    return fail(LOKI_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  CalibParams cp{};
+  cp.keys = keys;
+  cp.n = n;
+  const size_t s1_off = calib_part_bytes(sh, n, &cp.nch);
+  cp.part_s2 = static_cast<float*>(workspace);
+  cp.part_s1 = reinterpret_cast<float*>(static_cast<char*>(workspace) + s1_off);
+  cp.P = P;
+  cp.variances = variances;
+  cp.sh = sh;
+  return hip_status(launch_calibrate(cp, (hipStream_t)stream), "calibrate");
+}
+
 }  // extern "C"

@@ -87,6 +87,19 @@ struct PrefillParams {
   Shape sh;
 };
 
+struct CalibParams {
+  const void* keys;     // [Hkv, n, D] storage dtype, unrotated calibration keys
+  int n, nch;           // keys per head; chunks of kCalChunk keys
+  float* part_s2;       // [Hkv, nch, D, D] partial sums of y y^T (y = key - first key)
+  float* part_s1;       // [Hkv, nch, D] partial sums of y
+  float* P;             // [Hkv, D, D] principal directions as columns
+  float* variances;     // [Hkv, D] nullable
+  Shape sh;
+};
+
+// Calibration keys summed by one covariance workgroup.
+constexpr int kCalChunk = 2048;
+
 struct LayoutParams {
   const void* src;
   void* dst;
@@ -101,6 +114,7 @@ hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st);
 hipError_t launch_attend(const AttendParams& p, hipStream_t st);
 hipError_t launch_layout(const LayoutParams& p, hipStream_t st);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t st);
+hipError_t launch_calibrate(const CalibParams& p, hipStream_t st);
 
 // One-launch decode step (rotation, scores, top-k, attention) for shapes whose
 // per-unit scores fit the workgroup's LDS budget.

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for n in ["loki_decode", "loki_decode_append", "loki_append", "loki_rotate_query",
               "loki_score", "loki_topk", "loki_attend", "loki_pack_kcache", "loki_unpack_kcache",
               "loki_workspace_bytes", "loki_kcache_elems", "loki_strerror", "loki_last_error",
-              "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention"]:
+              "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention",
+              "loki_calibrate_workspace_bytes", "loki_calibrate"]:
         assert n in names
 
 
@@ -143,6 +144,16 @@ def test_other_entry_points_validate(L):
     assert pa(fake, fake, fake, fake, 32, None, cd, fake, 1 << 30, None) == -1   # out NULL
     assert pa(fake, fake, fake, fake, 32, fake, cd, fake, 16, None) == -3        # workspace
     assert pa(fake, fake, fake, fake, 32, fake, None, fake, 1 << 30, None) == -1  # desc NULL
+    nb = ctypes.c_size_t()
+    assert lib.loki_calibrate_workspace_bytes(cd, 5000, ctypes.byref(nb)) == 0
+    D, Hkv = d.head_dim, d.n_kv_heads
+    assert nb.value >= Hkv * 3 * (D * D + D) * 4                        # 3 chunks of 2048 keys
+    assert lib.loki_calibrate_workspace_bytes(cd, 0, ctypes.byref(nb)) == -1
+    cal = lib.loki_calibrate
+    assert cal(fake, 0, fake, None, cd, fake, 1 << 30, None) == -1      # n = 0
+    assert cal(None, 10, fake, None, cd, fake, 1 << 30, None) == -1     # keys NULL
+    assert cal(fake, 10, fake, odd, cd, fake, 1 << 30, None) == -1      # misaligned variances
+    assert cal(fake, 5000, fake, None, cd, fake, 1024, None) == -3      # workspace
     pf = lib.loki_prefill
     assert pf(fake, None, 129, 0, fake, fake, None, cd, None) == -1     # past S_cap
     assert pf(fake, None, 100, 29, fake, fake, None, cd, None) == -1    # pos + n past S_cap

@@ -584,6 +584,45 @@ def test_pca_attention_full_size(L):
     assert np.all(np.isfinite(out))
 
 
+# ------------------------------------------------------------- calibration
+
+@pytest.mark.parametrize("dtype,Hkv,n,D,offset", [
+    ("f16", 40, 8192, 128, 0.0), ("bf16", 3, 5000, 128, 3.0), ("f32", 2, 3000, 64, 1.0),
+    ("f16", 2, 100, 128, 0.5)])
+def test_calibrate(L, dtype, Hkv, n, D, offset):
+    """PCA of calibration keys on the GPU against the oracle's fp64 PCA."""
+    wl = _small(dtype, Hq=Hkv, Hkv=Hkv, D=D, S=64, k=8)
+    H.log(f"calibrate {dtype} Hkv={Hkv} n={n} D={D} offset={offset}")
+    keys = np.stack([W.draw_keys(W.rng(0, wl.wid, 1, kv), n, W.basis(wl, kv), W.sigma(wl))
+                     for kv in range(Hkv)]) + offset
+    keys = W.to_storage(keys, dtype)
+    desc = H.make_desc(wl, min(32, D))
+    P, var = L.calibrate(H.to_device(keys, dtype), desc)
+    torch.cuda.synchronize()
+    P = P.cpu().numpy().astype(np.float64)
+    var = var.cpu().numpy().astype(np.float64)
+    Pr, vr = oracle.calibrate(keys, dtype)
+    lam0 = vr[:, :1]
+    # eigenvalues: fp32-level error relative to the largest
+    assert np.all(np.abs(var - vr) <= 1e-5 * lam0), np.abs(var - vr).max()
+    # eigenvectors, up to sign: a vector is fixed only as far as its eigenvalue
+    # gap allows (perturbation of the matrix / gap)
+    gap = np.minimum(np.abs(np.diff(vr, prepend=np.inf, axis=1)),
+                     np.abs(np.diff(vr, append=-np.inf, axis=1)))
+    err = np.minimum(np.linalg.norm(P - Pr, axis=1), np.linalg.norm(P + Pr, axis=1))
+    tol = 1e-5 + 1e-5 * lam0 / np.maximum(gap, 1e-300)
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    H.log(f"  worst eigenvector err/tol {err[worst] / tol[worst]:.3f} at {worst}, "
+          f"max eigenvalue err {np.abs(var - vr).max() / lam0.max():.2e}")
+    assert np.all(err <= tol)
+    # the GPU's own output: orthonormal columns, signs by the first largest entry
+    for kv in range(Hkv):
+        assert np.abs(P[kv].T @ P[kv] - np.eye(D)).max() < 1e-5
+        lead = np.argmax(np.abs(P[kv]), axis=0)
+        assert np.all(P[kv][lead, np.arange(D)] > 0)
+        assert np.all(np.diff(var[kv]) <= 0)
+
+
 # ------------------------------------------------------------- Exact-TopK
 
 @pytest.mark.parametrize("dtype,g", [("f16", 1), ("bf16", 4)])
