@@ -286,8 +286,14 @@ def main():
                "frac_hbm_peak": round(prefill_bytes / (prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                "copy_same_bytes_us": round(copy_us, 2),
                "frac_of_copy_rate": round(copy_us / prefill_us, 4)}
-    # calibration: PCA of n_calib keys per KV head on the GPU (offline step)
-    keys_cal = k_rows[0, :, :wl.n_calib].contiguous()
+    # calibration: PCA of n_calib seeded synthetic keys per KV head (the
+    # generator's spectrum) on the GPU, the offline step that yields P
+    gcal = torch.Generator(device=dev)
+    gcal.manual_seed(7)
+    sig = torch.from_numpy(W.sigma(wl)).to(dev, torch.float32)
+    keys_cal = (torch.randn((wl.Hkv, wl.n_calib, wl.D), generator=gcal, device=dev) * sig).to(tdt)
+    if tuple(keys_cal.shape) != (wl.Hkv, wl.n_calib, wl.D) or not keys_cal.is_contiguous():
+        raise RuntimeError("calibration keys must be [Hkv, n_calib, D] contiguous")
     P_cal = torch.empty_like(P)
     var_cal = torch.empty((wl.Hkv, wl.D), dtype=torch.float32, device=dev)
     nb = ctypes.c_size_t()
