@@ -31,7 +31,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPreThreads = 256;        // VALU kernel
 constexpr int kPreTile = 64;            // tokens per LDS tile
-constexpr int kPreTokensPerWG = 512;    // tokens per workgroup (VALU kernel)
 constexpr int kPreWaves = 8;            // MFMA kernel: waves per workgroup
 constexpr int kPreDepth = 2;            // MFMA kernel: key tiles in flight
 
@@ -200,9 +199,10 @@ __global__ __launch_bounds__(64 * NW, 1024 / (64 * NW)) void prefill_mfma_kernel
 }
 
 // Thread (slot, j) keeps column j of P[kv] in registers and forms coordinate j
-// of tokens slot, slot + NSLOT, ... of each run of RUN tokens staged in LDS.
+// of tokens slot, slot + NSLOT, ... of each run of RUN tokens staged in LDS;
+// a workgroup covers tpwg tokens.
 template <int DT, int D>
-__global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams p, int tpwg) {
   constexpr int NSLOT = kPreThreads / D, RUN = 32;
   __shared__ __align__(16) float xs[RUN][D];
   const Shape& sh = p.sh;
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams
 #pragma unroll
     for (int i = 0; i < D; i++) pc[i] = P[(size_t)i * D + j];
   }
-  const int t_begin = blockIdx.x * kPreTokensPerWG;
-  const int t_end = min(p.n_tokens, t_begin + kPreTokensPerWG);
+  const int t_begin = blockIdx.x * tpwg;
+  const int t_end = min(p.n_tokens, t_begin + tpwg);
   for (int t0 = t_begin; t0 < t_end; t0 += RUN) {
     __syncthreads();  // previous run consumed
     for (int e = threadIdx.x; e < RUN * D; e += kPreThreads) {
@@ -240,6 +240,24 @@ __global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams
   }
 }
 
+// Tokens per workgroup from a list of candidates: the largest whose whole
+// rounds of resident workgroups (a last partial round costs as much as a full
+// one) take least time, each workgroup costing its tokens plus `setup` tokens'
+// worth (loading its part of P).
+static int pick_tokens(const PrefillParams& p, int per_cu, const int* cand, int n_cand, int setup) {
+  const long long slots = (long long)per_cu * (p.cus > 0 ? p.cus : 256);
+  const long long heads = (long long)p.sh.B * p.sh.Hkv;
+  int best = 0;
+  long long best_cost = 0;
+  for (int i = 0; i < n_cand; i++) {
+    const int t = cand[i];
+    const long long wgs = (p.n_tokens + t - 1) / t * heads;
+    const long long cost = (wgs + slots - 1) / slots * (t + setup);
+    if (best == 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  return best;
+}
+
 template <int DT, int TPWG>
 hipError_t launch_mfma(const PrefillParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((p.n_tokens + TPWG - 1) / TPWG), (unsigned)(p.sh.B * p.sh.Hkv));
@@ -247,10 +265,6 @@ hipError_t launch_mfma(const PrefillParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tokens per workgroup: the largest of 4096 .. 512 whose whole rounds of
-// resident workgroups (a last partial round costs as much as a full one)
-// take least time, each workgroup costing its tokens plus a set-up of about
-// 128 tokens' worth (loading and splitting its columns of P).
 template <int DT>
 hipError_t launch_mfma_sized(const PrefillParams& p, hipStream_t st) {
   static const int per_cu = [] {
@@ -261,16 +275,8 @@ hipError_t launch_mfma_sized(const PrefillParams& p, hipStream_t st) {
       nb = 1;
     return nb;
   }();
-  const long long slots = (long long)per_cu * (p.cus > 0 ? p.cus : 256);
-  const long long heads = (long long)p.sh.B * p.sh.Hkv;
-  int best = 0;
-  long long best_cost = 0;
-  for (int t : {4096, 2048, 1024, 512}) {
-    const long long wgs = (p.n_tokens + t - 1) / t * heads;
-    const long long cost = (wgs + slots - 1) / slots * (t + 128);
-    if (best == 0 || cost < best_cost) best = t, best_cost = cost;
-  }
-  switch (best) {
+  static const int cand[] = {4096, 2048, 1024, 512};
+  switch (pick_tokens(p, per_cu, cand, 4, 128)) {
     case 4096: return launch_mfma<DT, 4096>(p, st);
     case 2048: return launch_mfma<DT, 2048>(p, st);
     case 1024: return launch_mfma<DT, 1024>(p, st);
@@ -278,18 +284,28 @@ hipError_t launch_mfma_sized(const PrefillParams& p, hipStream_t st) {
   }
 }
 
+template <int DT, int D>
+hipError_t launch_valu(const PrefillParams& p, hipStream_t st) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_valu_kernel<DT, D>, kPreThreads,
+                                                     0) != hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  static const int cand[] = {512, 256, 128, 64};
+  const int tpwg = pick_tokens(p, per_cu, cand, 4, 32);
+  const dim3 grid((unsigned)((p.n_tokens + tpwg - 1) / tpwg), (unsigned)(p.sh.B * p.sh.Hkv));
+  prefill_valu_kernel<DT, D><<<grid, kPreThreads, 0, st>>>(p, tpwg);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_dt(const PrefillParams& p, hipStream_t st) {
   if constexpr (DT != F32) {
     if (p.sh.D == 128) return launch_mfma_sized<DT>(p, st);
   }
-  const dim3 grid((unsigned)((p.n_tokens + kPreTokensPerWG - 1) / kPreTokensPerWG),
-                  (unsigned)(p.sh.B * p.sh.Hkv));
-  if (p.sh.D == 128)
-    prefill_valu_kernel<DT, 128><<<grid, kPreThreads, 0, st>>>(p);
-  else
-    prefill_valu_kernel<DT, 64><<<grid, kPreThreads, 0, st>>>(p);
-  return hipGetLastError();
+  return p.sh.D == 128 ? launch_valu<DT, 128>(p, st) : launch_valu<DT, 64>(p, st);
 }
 
 }  // namespace
