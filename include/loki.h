@@ -20,7 +20,7 @@
  *        KV-cache append is part of each step;
  *   [TB] same page, "More on tables", first table: k_f is the fraction of keys
  *        kept, d_f the fraction of the key dimensions used for scoring;
- *   [S]  same page, "More on figures": per-layer attention time of vanilla
+ *   [VA] same page, "More on figures": per-layer attention time of vanilla
  *        attention against Loki (Llama2-13B), the speed-up being measured;
  *   [PT] same page, "More on tables", the PCAAttn table: a Loki variant that
  *        attends with the reduced-dimensional scores directly;
@@ -221,7 +221,7 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
 
 /*
  * Dense decode attention over all S cached tokens, the baseline the pages
- * measure Loki against ([T] "TL;DR" and [S]: speed-up of Loki's attention
+ * measure Loki against ([T] "TL;DR" and [VA]: speed-up of Loki's attention
  * over vanilla attention): qr = q . P[kv], z_t = scale * qr . krot_t over all
  * D coordinates of every token t < S, out = softmax(z) . V.  Because P is
  * orthonormal, qr . krot_t = q . k_t: this is ordinary full attention, read
