@@ -93,8 +93,8 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
     for (int q = 0; q < RB; q++) {
       const int r = rbase + q * NG;
       const int t = r < nr ? sidx[r] : -1;
-      kb[q] = load16(krs, (t >= 0 && k_needed) ? k_base + (uint32_t)t * k_row_bytes : kOutOfRange);
-      vb[q] = load16(vrs, t >= 0 ? ((uint32_t)t * D + j0) * EB : kOutOfRange);
+      kb[q] = load16_stream(krs, (t >= 0 && k_needed) ? k_base + (uint32_t)t * k_row_bytes : kOutOfRange);
+      vb[q] = load16_stream(vrs, t >= 0 ? ((uint32_t)t * D + j0) * EB : kOutOfRange);
     }
   };
   auto consume = [&](const u32x4 (&kb)[RB], const u32x4 (&vb)[RB], int rbase) {

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
     for (int it = 0; it < NB; it++) {
       const int t = (pass0 + it) * TPP + tl;
-      x[it] = load16(prs, t < S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+      x[it] = load16_stream(prs, t < S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
     }
   };
   u32x4 xa[NB], xb[NB];

@@ -113,6 +113,12 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
+// Same, with the nontemporal cache policy: for data read once (cache
+// streams); on MI355X a read stream with it runs at ~7.0 TB/s against
+// ~6.2 TB/s with the default policy.
+__device__ __forceinline__ u32x4 load16_stream(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
+}
 
 // ---------------------------------------------------------------- cross-lane
 

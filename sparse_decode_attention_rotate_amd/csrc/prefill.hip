@@ -103,7 +103,8 @@ __global__ __launch_bounds__(64 * NW, 1024 / (64 * NW)) void prefill_mfma_kernel
 #pragma unroll
     for (int u = 0; u < CPT; u++) {
       const int c = tid + u * NT, t = t0 + c / 16;
-      x[u] = t < t_end ? *reinterpret_cast<const u32x4*>(krow + (size_t)t * D + (c % 16) * 8)
+      x[u] = t < t_end ? __builtin_nontemporal_load(
+                             reinterpret_cast<const u32x4*>(krow + (size_t)t * D + (c % 16) * 8))
                        : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -185,8 +186,10 @@ __global__ __launch_bounds__(64 * NW, 1024 / (64 * NW)) void prefill_mfma_kernel
         const size_t row = (size_t)(p.pos + t);
         const size_t e0 = j0 < sh.dp ? row * sh.dp + j0
                                      : sh.kl.rest_off + row * sh.kl.rest + (j0 - sh.dp);
-        *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(p.kcache) + head * sh.kl.head_elems +
-                                  e0) = *reinterpret_cast<const u32x4*>(&ot[tt][j0]);
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(&ot[tt][j0]),
+            reinterpret_cast<u32x4*>(static_cast<unsigned short*>(p.kcache) +
+                                     head * sh.kl.head_elems + e0));
       }
     }
   };

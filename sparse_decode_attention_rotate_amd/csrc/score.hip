@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
 #pragma unroll
     for (int it = 0; it < NB; it++) {
       const int t = t0 + (pass0 + it) * TPP + tl;
-      x[it] = load16(prs, t < t_end ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+      x[it] = load16_stream(prs, t < t_end ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
     }
   };
   u32x4 xa[NB], xb[NB];

@@ -266,28 +266,66 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
 
   select_scan<NT>(sm, k);
   const int bstar = sm.sel_bin;
-  const int rem = k - sm.sel_gt;  // 1 <= rem <= members of b*
-  const int nb = sm.sel_eq;
+  const int rem0 = k - sm.sel_gt;  // 1 <= rem0 <= members of b*
+  int rem = rem0, nb = sm.sel_eq;
 
-  // ---- 2. the last taken element (T, I) inside b*, and the number of taken
-  // elements of each wave's index range in sm.wcnt
+  // ---- 1c. a crowded b* (a wide score range, e.g. a few large outliers,
+  // squeezes the bulk into few bins): split b*'s interval linearly into kBins
+  // sub-bins -- monotone in the score, so the order is kept -- and find the
+  // sub-bin holding the rem-th largest member.  sub < 0: not refined.
+  int sub = -1;
+  float lo2 = 0.f, scale2 = 0.f;
+  if (nb > kFewCandidates && scale > 0.f && scale * (float)kBins < INFINITY) {
+    lo2 = lo + (float)bstar / scale;
+    scale2 = scale * (float)kBins;
+    for (int e = tid; e < kBins; e += NT) sm.hist[e] = 0u;
+    __syncthreads();  // every thread has read the first scan's results
+    row.each([&](int i, unsigned key) {
+      const float sc = key_score(key);
+      if (i < S && lin_bin(sc, lo, scale) == bstar) atomicAdd(&sm.hist[lin_bin(sc, lo2, scale2)], 1u);
+    });
+    __syncthreads();
+    select_scan<NT>(sm, rem0);
+    sub = sm.sel_bin;
+    rem = rem0 - sm.sel_gt;
+    nb = sm.sel_eq;
+  }
+  // position of a key against the threshold group: 1 above, 0 inside, -1 below
+  auto side = [&](unsigned key) -> int {
+    const float sc = key_score(key);
+    const int bn = lin_bin(sc, lo, scale);
+    if (bn != bstar) return bn > bstar ? 1 : -1;
+    if (sub < 0) return 0;
+    const int sb = lin_bin(sc, lo2, scale2);
+    return sb > sub ? 1 : (sb == sub ? 0 : -1);
+  };
+
+  // ---- 2. the last taken element (T, I) inside the threshold group, and the
+  // number of taken elements of each wave's index range in sm.wcnt
   if (nb <= kFewCandidates) {
-    // one pass: members of b* become candidates, members of higher bins are
+    // one pass: members of the group become candidates, members above it are
     // counted per wave
     unsigned gt = 0u;
-    row.each([&](int i, unsigned key) {
-      const int bn = lin_bin(key_score(key), lo, scale);
+    auto visit = [&](int i, unsigned key, int sd) {
       const bool valid = i < S;
-      gt += (unsigned)__popcll(__ballot(valid && bn > bstar));
-      const bool cand = valid && bn == bstar;
-      if (__ballot(cand) != 0ull) {  // rare: this wave row holds members of b*
+      gt += (unsigned)__popcll(__ballot(valid && sd > 0));
+      const bool cand = valid && sd == 0;
+      if (__ballot(cand) != 0ull) {  // rare: this wave row holds members of the group
         if (cand) {
           const int slot = atomicAdd(&sm.n_cand, 1);
           sm.cand_key[slot] = key;
           sm.cand_idx[slot] = i;
         }
       }
-    });
+    };
+    if (sub < 0) {
+      row.each([&](int i, unsigned key) {
+        const int bn = lin_bin(key_score(key), lo, scale);
+        visit(i, key, bn > bstar ? 1 : (bn == bstar ? 0 : -1));
+      });
+    } else {
+      row.each([&](int i, unsigned key) { visit(i, key, side(key)); });
+    }
     if (lane == 0) sm.wcnt[wave] = (int)gt;
     __syncthreads();
     if (wave == 0) {
@@ -310,7 +348,7 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     __syncthreads();
   } else {
-    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm);
+    radix_threshold<NT, KREG>(row, bstar, rem0, lo, scale, sm);
     const unsigned Tk = sm.thr_key;
     const int Ik = sm.thr_idx;
     int cnt = 0;

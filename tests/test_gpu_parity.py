@@ -291,6 +291,20 @@ def _topk_cases():
         row[g.choice(4096, 6, replace=False)] = kth
     cases.append(("dup-at-threshold", dup, 512))
     cases.append(("dup-at-threshold-16k", np.tile(dup[:, :4096], (1, 4)) * 1.0, 2048))
+    # a few huge outliers squeeze the bulk into few linear bins: the crowded
+    # threshold bin is refined once (1e3, 1e4) or, still crowded, resolved by
+    # radix passes (1e7); with duplicates of the k-th value as well
+    for scale_out, S, k in [(1e3, 4096, 512), (1e4, 32768, 4096), (1e7, 32768, 4096),
+                            (1e4, 16384, 2048)]:
+        o = g.standard_normal((3, S)).astype(np.float32)
+        pos = g.choice(S, max(1, S // 1000), replace=False)
+        o[:, pos] = (np.sign(g.standard_normal(pos.size)) * scale_out).astype(np.float32)
+        cases.append((f"outliers-{scale_out:g}-{S}-{k}", o, k))
+    od = cases[-1][1].copy()
+    for row in od:
+        kth = np.sort(row)[::-1][2047]
+        row[g.choice(16384, 9, replace=False)] = kth
+    cases.append(("outliers-dup-at-threshold", od, 2048))
     return cases
 
 
