@@ -131,7 +131,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
     for (int it = 0; it < NB; it++) {
       const int t = (pass0 + it) * TPP + tl;
-      x[it] = load16_stream(prs, t < S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+      const uint32_t off = t < S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
+      // a unit with a helper keeps its panel in L2 for the helper's second read
+      x[it] = paired ? load16(prs, off) : load16_stream(prs, off);
     }
   };
   u32x4 xa[NB], xb[NB];
