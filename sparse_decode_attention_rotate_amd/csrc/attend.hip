@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kAttThreads = 256;
 
-template <int DT, int D, bool SPLIT, bool LOW>
+template <int DT, int D, bool SPLIT, bool LOW, bool STREAM>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __shared__ int sidx[kAttendChunk];
   __shared__ float slow[kAttendChunk];
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __syncthreads();
 
   float M, L, A;
-  block_attend<DT, D, kAttThreads, SPLIT, kRowsPerBatch, LOW>(
+  block_attend<DT, D, kAttThreads, SPLIT, kRowsPerBatch, LOW, STREAM>(
       p.qr + bh * D, p.scale_log2, sidx, slow, nr, p.kcache, p.vcache, head, sh, sm, M, L, A, p.d);
   if (tid < D) {
     if (p.nsplit == 1) {
@@ -83,12 +83,25 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
 template <int DT, int D>
 hipError_t launch_d(const AttendParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.nsplit * p.sh.B * p.sh.Hq));
-  if (p.sel_scores)
-    attend_kernel<DT, D, true, false><<<grid, kAttThreads, 0, st>>>(p);
-  else if (p.low_dim)
-    attend_kernel<DT, D, false, true><<<grid, kAttThreads, 0, st>>>(p);
-  else
-    attend_kernel<DT, D, false, false><<<grid, kAttThreads, 0, st>>>(p);
+  // one query head per KV head: every row is read once (streamed); grouped
+  // heads share rows through L2
+  const bool once = p.sh.g == 1;
+  if (p.sel_scores) {
+    if (once)
+      attend_kernel<DT, D, true, false, true><<<grid, kAttThreads, 0, st>>>(p);
+    else
+      attend_kernel<DT, D, true, false, false><<<grid, kAttThreads, 0, st>>>(p);
+  } else if (p.low_dim) {
+    if (once)
+      attend_kernel<DT, D, false, true, true><<<grid, kAttThreads, 0, st>>>(p);
+    else
+      attend_kernel<DT, D, false, true, false><<<grid, kAttThreads, 0, st>>>(p);
+  } else {
+    if (once)
+      attend_kernel<DT, D, false, false, true><<<grid, kAttThreads, 0, st>>>(p);
+    else
+      attend_kernel<DT, D, false, false, false><<<grid, kAttThreads, 0, st>>>(p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   combine_kernel<D><<<dim3((unsigned)(p.sh.B * p.sh.Hq)), D, 0, st>>>(p);

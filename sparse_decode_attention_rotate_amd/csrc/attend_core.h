@@ -49,7 +49,11 @@ struct AttendSmem {
 // head: flattened (b, kv) of the caches.  On return thread tid < D holds the
 // merged (M, L, A) with A the unnormalised output coordinate tid, in the log2
 // domain: out[tid] = A / L.
-template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch, bool LOW = false>
+// STREAM: the rows are read once (one query head per KV head): nontemporal
+// loads; else (several query heads read the same rows) default-policy loads,
+// which keep the rows in L2 for the other heads.
+template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch, bool LOW = false,
+          bool STREAM = true>
 __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2,
                                              const int* sidx, const float* slow, int nr,
                                              const void* kcache, const void* vcache,
@@ -93,8 +97,10 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
     for (int q = 0; q < RB; q++) {
       const int r = rbase + q * NG;
       const int t = r < nr ? sidx[r] : -1;
-      kb[q] = load16_stream(krs, (t >= 0 && k_needed) ? k_base + (uint32_t)t * k_row_bytes : kOutOfRange);
-      vb[q] = load16_stream(vrs, t >= 0 ? ((uint32_t)t * D + j0) * EB : kOutOfRange);
+      const uint32_t ko = (t >= 0 && k_needed) ? k_base + (uint32_t)t * k_row_bytes : kOutOfRange;
+      const uint32_t vo = t >= 0 ? ((uint32_t)t * D + j0) * EB : kOutOfRange;
+      kb[q] = STREAM ? load16_stream(krs, ko) : load16(krs, ko);
+      vb[q] = STREAM ? load16_stream(vrs, vo) : load16(vrs, vo);
     }
   };
   auto consume = [&](const u32x4 (&kb)[RB], const u32x4 (&vb)[RB], int rbase) {

@@ -402,7 +402,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     // pair j: owner's at help_part[2j], helper's at help_part[2j+1].
     const int r0 = helper ? p.k0 : 0, nr = helper ? k - p.k0 : p.k0;
     float M, L, A;
-    block_attend<DT, D, NT, true, kFusedRowsPerBatch>(qs[0], p.scale_log2, sidx + r0, slow + r0,
+    block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, G == 1>(qs[0], p.scale_log2, sidx + r0, slow + r0,
                                                       nr, p.kcache, p.vcache, head, sh, asm_, M,
                                                       L, A);
     float* mine = p.help_part + ((size_t)pair * 2 + (helper ? 1 : 0)) * (D + 2);
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   }
   for (int h = 0; h < G; h++) {
     float M, L, A;
-    block_attend<DT, D, NT, true, kFusedRowsPerBatch>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
+    block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, G == 1>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
                                   p.kcache, p.vcache, head, sh, asm_, M, L, A);
     if (tid < D) p.out[(q0 + h) * D + tid] = A / L;
     __syncthreads();  // asm_ is reused by the next head
