@@ -23,6 +23,7 @@ namespace loki {
 namespace {
 
 constexpr int kAttThreads = 256;
+constexpr int kXcds = 8;  // MI355X: workgroup i runs on XCD i % 8
 
 template <int DT, int D, bool SPLIT, bool LOW, bool STREAM>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
@@ -31,8 +32,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __shared__ AttendSmem<DT, D, kAttThreads> sm;
 
   const Shape& sh = p.sh;
-  const int split = blockIdx.x % p.nsplit;
-  const size_t bh = blockIdx.x / p.nsplit;
+  // Grouped heads gathering selected rows share them through L2, one per
+  // XCD: workgroups are dealt to the 8 XCDs round-robin by index, so the
+  // g * nsplit workgroups of one (b, kv) group are given indices that fall on
+  // the same XCD.  (Without index lists -- every token -- the plain order
+  // already puts the g heads of one chunk on one XCD at the same time.)
+  int wg = (int)blockIdx.x;
+  if (!STREAM && p.idx) {
+    const int per = sh.g * p.nsplit;
+    const int x = wg % kXcds, s = wg / kXcds;
+    wg = ((s / per) * kXcds + x) * per + s % per;
+    if (wg >= p.nsplit * sh.B * sh.Hq) return;  // padding of the last groups
+  }
+  const int split = wg % p.nsplit;
+  const size_t bh = (size_t)(wg / p.nsplit);
   const int b = (int)(bh / sh.Hq), h = (int)(bh % sh.Hq);
   const size_t head = (size_t)b * sh.Hkv + h / sh.g;
   const int r0 = split * p.kc;
@@ -82,7 +95,13 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
 
 template <int DT, int D>
 hipError_t launch_d(const AttendParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.nsplit * p.sh.B * p.sh.Hq));
+  // grouped heads with index lists: whole groups of kXcds (b, kv) units, so
+  // that each XCD gets the workgroups of its groups (the padding workgroups
+  // return at once)
+  const size_t groups = (size_t)p.sh.B * p.sh.Hkv;
+  const dim3 grid((unsigned)(p.sh.g == 1 || !p.idx
+                                 ? (size_t)p.nsplit * p.sh.B * p.sh.Hq
+                                 : (groups + kXcds - 1) / kXcds * kXcds * p.sh.g * p.nsplit));
   // one query head per KV head: every row is read once (streamed); grouped
   // heads share rows through L2
   const bool once = p.sh.g == 1;

@@ -91,6 +91,37 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       }
       return;
     }
+    if constexpr ((G == 4 || G == 2) && LPT == 4) {
+      // reduce-scatter over the heads: after the pair and quad exchanges
+      // lane c holds the whole score of head c (G = 4) or of head c % 2
+      // (G = 2, stored by lanes 0 and 1)
+      const bool b0 = (c & 1) != 0, b1 = (c & 2) != 0;
+#pragma unroll
+      for (int it = 0; it < NB; it++) {
+        float f[E];
+        unpack16<DT>(x[it], f);
+        float a[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; e++) acc = fmaf(qv[h][e], f[e], acc);
+          a[h] = acc;
+        }
+        float r;
+        if constexpr (G == 4) {
+          const float u0 = (b0 ? a[1] : a[0]) + dpp_f<0xB1>(b0 ? a[0] : a[1]);
+          const float u1 = (b0 ? a[3] : a[2]) + dpp_f<0xB1>(b0 ? a[2] : a[3]);
+          r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
+        } else {
+          const float u = (b0 ? a[1] : a[0]) + dpp_f<0xB1>(b0 ? a[0] : a[1]);
+          r = u + dpp_f<0x4E>(u);
+        }
+        const int t = t0 + (pass0 + it) * TPP + tl;
+        if (t < t_end && c < G) srow[(size_t)c * sh.S + t] = r;
+      }
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < NB; it++) {
       float f[E];
@@ -141,10 +172,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
 template <int DT, int LPT>
 hipError_t launch_lpt(ScoreParams p, hipStream_t st) {
   // tiles of up to 4096 tokens (256 KB of an fp16 panel), smaller when that
-  // leaves fewer than two workgroups per compute unit; multiples of two batches
+  // leaves fewer than two workgroups per compute unit (eight when a tile also
+  // writes the scores of several heads); multiples of two batches
   constexpr int STEP = (kScoreThreads / LPT) * 2 * kScoreBatch;
   const long long units = (long long)p.sh.B * p.sh.Hkv;
-  long long want = (long long)p.sh.S * units / 512;
+  long long want = (long long)p.sh.S * units / (p.sh.g > 1 ? 2048 : 512);
   want = want < STEP ? STEP : (want > 4096 ? 4096 : want);
   p.tile_tokens = (int)((want + STEP - 1) / STEP * STEP);
   p.n_tiles = (p.sh.S + p.tile_tokens - 1) / p.tile_tokens;
