@@ -32,13 +32,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   __shared__ AttendSmem<DT, D, kAttThreads> sm;
 
   const Shape& sh = p.sh;
-  // Grouped heads gathering selected rows share them through L2, one per
-  // XCD: workgroups are dealt to the 8 XCDs round-robin by index, so the
-  // g * nsplit workgroups of one (b, kv) group are given indices that fall on
-  // the same XCD.  (Without index lists -- every token -- the plain order
-  // already puts the g heads of one chunk on one XCD at the same time.)
+  // Grouped heads gathering selected rows: workgroups are dealt to the 8 XCDs
+  // round-robin by index, so the g * nsplit workgroups of one (b, kv) group
+  // are given indices that fall on the same XCD, where the rows the heads
+  // share meet in one L2.  (Without index lists -- every token -- the plain
+  // order already puts the g heads of one chunk on one XCD at the same time.)
   int wg = (int)blockIdx.x;
-  if (!STREAM && p.idx) {
+  if (sh.g > 1 && p.idx) {
     const int per = sh.g * p.nsplit;
     const int x = wg % kXcds, s = wg / kXcds;
     wg = ((s / per) * kXcds + x) * per + s % per;
@@ -102,9 +102,12 @@ hipError_t launch_d(const AttendParams& p, hipStream_t st) {
   const dim3 grid((unsigned)(p.sh.g == 1 || !p.idx
                                  ? (size_t)p.nsplit * p.sh.B * p.sh.Hq
                                  : (groups + kXcds - 1) / kXcds * kXcds * p.sh.g * p.nsplit));
-  // one query head per KV head: every row is read once (streamed); grouped
-  // heads share rows through L2
-  const bool once = p.sh.g == 1;
+  // Load policy: index lists are streamed (nontemporal) -- grouped heads
+  // select mostly different rows (their sets overlap by ~15-20% here), so the
+  // stream rate is worth more than the reuse; every token with grouped heads
+  // keeps the default policy, so that the g heads reading each chunk share it
+  // in L2.
+  const bool once = p.sh.g == 1 || p.idx != nullptr;
   if (p.sel_scores) {
     if (once)
       attend_kernel<DT, D, true, false, true><<<grid, kAttThreads, 0, st>>>(p);
