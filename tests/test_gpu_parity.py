@@ -404,6 +404,12 @@ E2E = {
     "gqa4-bf16": dict(dtype="bf16", Hq=8, Hkv=2, S=5000, k=700),
     "gqa8-f16": dict(dtype="f16", Hq=16, Hkv=2, S=2100, k=130),
     "gqa3-generic": dict(dtype="f16", Hq=6, Hkv=2, S=1100, k=100),
+    # grouped heads inside the one-launch kernel (g = 2, 4; their scores and
+    # index lists fit its LDS budget)
+    "gqa2-fused-f16": dict(dtype="f16", B=3, Hq=8, Hkv=4, S=3000, k=300),
+    "gqa4-fused-bf16": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=1800, k=200),
+    "gqa2-fused-f32": dict(dtype="f32", B=2, Hq=4, Hkv=2, S=2222, k=222, tau=20.0),
+    "gqa4-fused-k1": dict(dtype="f16", B=2, Hq=8, Hkv=2, S=1000, k=1),
     "d-below-panel": dict(dtype="f16", d=20),
     "d-above-panel": dict(dtype="f16", d=48),
     "d-full": dict(dtype="f16", d=128),
@@ -425,6 +431,8 @@ def test_decode_end_to_end(L, case, separate):
     x = W.generate(wl)
     dev = H.upload(wl, x)
     plan = L.decode_plan(dev["desc"], wl.d, wl.k, wl.append)
+    if "fused" in case:
+        assert plan, f"{case} is meant to take the one-launch kernel"
     H.log(f"decode {case} separate={separate} one_launch={plan}: {W.describe(wl)}")
     out, idx = H.run_decode(wl, dev, separate=separate)
     res = H.full_parity(wl, x, out, idx)
