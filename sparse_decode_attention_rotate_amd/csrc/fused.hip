@@ -34,10 +34,7 @@ namespace {
 constexpr int kFusedMaxS = 4096;          // scores of a unit held in registers for select
 constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per batch
 constexpr size_t kFusedDynBytes = 36 * 1024;
-#ifndef LOKI_FUSED_RB
-#define LOKI_FUSED_RB 4
-#endif
-constexpr int kFusedRowsPerBatch = LOKI_FUSED_RB;  // gather rows per lane group per batch
+constexpr int kFusedRowsPerBatch = 4;  // gather rows per lane group per batch
 
 // Words exchanged between the two workgroups of a paired unit are accessed
 // only with agent-coherent loads and stores (relaxed agent-scope atomics,
