@@ -139,6 +139,8 @@ def full_parity(wl: W.Workload, x: dict, out_gpu, idx_gpu, d=None, k=None, heads
     d = wl.d if d is None else d
     k = wl.k if k is None else k
     krot, v = oracle_inputs_after_append(wl, x)
+    # the step reads the S cached tokens; rows past S are spare capacity
+    krot, v = krot[:, :, :wl.S], v[:, :, :wl.S]
     r = oracle.decode(x["q"], krot, v, x["P"], d, k, wl.dtype, heads=heads)
     n, n_diff, n_swaps = check_index_sets(idx_gpu, r["scores"], k, heads)
     ref = oracle.attend_given(x["q"], krot, v, x["P"], idx_gpu, wl.dtype, heads=heads)
