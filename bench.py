@@ -310,6 +310,35 @@ def main():
                    "covariance_GFLOP": round(2.0 * wl.Hkv * wl.n_calib * wl.D * wl.D / 1e9, 3)}
     del k_rows, kc_p, cp_dst, keys_cal, ws_cal
 
+    # the appending step on the same shape: one new token per (b, kv) written
+    # at row S-1 of each cache copy, then the decode over the S tokens.  The new
+    # key and value are seeded draws with the keys' per-coordinate spread; the
+    # timing does not depend on their values beyond the selection.  Last, since
+    # it rewrites row S-1 of the cycled copies.
+    append_step = None
+    if not wl.append:
+        gnew = torch.Generator(device=dev)
+        gnew.manual_seed(11)
+        kn_t = (torch.randn((wl.B, wl.Hkv, wl.D), generator=gnew, device=dev) * sig).to(tdt)
+        vn_t = torch.randn((wl.B, wl.Hkv, wl.D), generator=gnew, device=dev).to(tdt)
+        kn_, vn_ = vp(kn_t.data_ptr()), vp(vn_t.data_ptr())
+
+        def append_call(i, cd_):
+            chk(lib.loki_decode_append(q_, kn_, vn_, kcs[i % len(kcs)], vcs[i % len(vcs)], P_,
+                                       wl.d, wl.k, out_, None, cd_, ws_, ws.numel(), st))
+
+        # the decode step timed again just before, under the same conditions
+        dec_us = timed(lambda i: step(i))
+        app_us = timed(lambda i: append_call(i, cd))
+        app_sep_us = timed(lambda i: append_call(i, ctypes.byref(cdesc_sep)))
+        append_step = {"us_per_step": round(app_us, 2),
+                       "launch_plan": ("one kernel" if loki.decode_plan(desc, wl.d, wl.k, True)
+                                       else "separate kernels"),
+                       "decode_us_alongside": round(dec_us, 2),
+                       "over_decode_us": round(app_us - dec_us, 2),
+                       "separate_launches_us": round(app_sep_us, 2)}
+        del kn_t, vn_t
+
     es = 4 if wl.dtype == "f32" else 2
     alg_bytes = wl.algorithmic_bytes()
     score_bytes = es * wl.B * wl.Hkv * wl.S * wl.d
@@ -354,6 +383,7 @@ def main():
         "pca_attention": pca,
         "prefill": prefill,
         "calibration": calibration,
+        "append_step": append_step,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

@@ -122,8 +122,8 @@ int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes);
  * or loki_decode_append (append = 1) with these arguments runs as a single
  * kernel (rotation, scores in LDS, top-k, attention per (b, kv) workgroup:
  * needs d == panel_dim, head_dim 128, Hq/Hkv in {1, 2, 4}, S <= 4096 and the
- * group's scores within the LDS budget, no append), 0 when it runs as separate
- * launches.
+ * group's scores within the LDS budget; the same conditions with or without
+ * append), 0 when it runs as separate launches.
  */
 int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_launch);
 
@@ -212,7 +212,13 @@ int loki_decode(const void* q, const void* kcache, const void* vcache, const flo
 /*
  * Append then decode [C], [F1]: appends (k_new, v_new) at row pos = S-1 as
  * loki_append does, then runs loki_decode over the S tokens (the new one
- * included).  The append shares the query-rotation launch.
+ * included).  k_new, v_new [B, Hkv, D] storage dtype.  As separate launches
+ * the append shares the query-rotation launch; as one launch (see
+ * loki_decode_plan) the kernel rotates and writes row S-1 itself and scores
+ * the new token from the rounded row it wrote.  Either way row S-1 of both
+ * caches holds the appended token on return; the rotated key may differ from
+ * loki_append's in the last place of an element (a different fp32 summation
+ * order before the rounding).
  */
 int loki_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
                        void* vcache, const float* P, int d, int k, float* out,

@@ -21,6 +21,19 @@
 // A decode step becomes one kernel: no launch gaps, no ramp-up/drain between
 // phases, and the scores never leave LDS.  Used when d == dp, the unit's g
 // score rows fit the LDS budget and S <= 4096.
+//
+// The appending variant (poster page, "Loki's Computational Cost": the
+// KV-cache append belongs to every step) also takes the step's new key and
+// value as token S-1: the key is rotated as one more row of phases 0 and 0'
+// (same P loads), rounded to the storage dtype and written to row S-1 of the
+// cache, the value row is copied, and the panel stream stops at S-1.  The new
+// token's score comes from the rounded key in LDS with the lane partials and
+// pairwise sums of the panel stream, so it is the score a later step computes
+// from the stored row; no wave reads row S-1 of the panel.  Every wave waits
+// for its stores before the barrier ahead of the attention, whose gathers may
+// read the new row.
+#include <type_traits>
+
 #include "attend_core.h"
 #include "loki_internal.h"
 #include "select_core.h"
@@ -54,8 +67,9 @@ __device__ __forceinline__ float ld_coherent(const float* a) {
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
-template <int DT, int D, int LPT, int G, int NT>
+template <int DT, int D, int LPT, int G, int NT, bool APPEND>
 __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParams p) {
+  constexpr int GR = G + (APPEND ? 1 : 0);  // rows rotated: the queries, then the new key
   constexpr int NW = NT / 64;
   constexpr int KREG = kFusedMaxS / NT;  // order keys per thread in the selection
   constexpr int E = Elem<DT>::kPerVec;
@@ -67,18 +81,21 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   // rotation of the remaining coordinates: 32 quad slots x 8 row slots
   constexpr int NQR = (D - DP) / 4, RSR = NT / 32, NR = D / RSR;
   static_assert(NT % NQL == 0 && D % RSL == 0 && NQR <= 32 && D % RSR == 0, "rotation tiling");
+  static_assert(G * LPT <= 64, "the new token's score is formed by one wave");
 
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SelectSmem<NW> ssm;
   __shared__ AttendSmem<DT, D, NT> asm_;
-  __shared__ float xq[G][D];             // query rows, fp32
-  __shared__ float qpart[NW][G][D];      // per-wave partial rotations
+  __shared__ float xq[GR][D];            // query rows (and the new key), fp32
+  __shared__ float qpart[NW][GR][D];     // per-wave partial rotations
   __shared__ float qs[G][D];             // rotated query rows
+  __shared__ float kn[APPEND ? D : 1];   // rotated new key as stored
   __shared__ float rng[2][NW][G];        // per-wave score min / max
   __shared__ int later;                  // paired unit: this workgroup merges the halves
 
   const Shape& sh = p.sh;
   const int S = sh.S, k = p.k;
+  const int Ss = APPEND ? S - 1 : S;  // tokens read from the panel
   float* sc = reinterpret_cast<float*>(dyn);             // [G][S]
   int* sidx = reinterpret_cast<int*>(sc + G * S);        // [G][k]
   float* slow = reinterpret_cast<float*>(sidx + G * k);  // [G][k]
@@ -110,11 +127,15 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   u32x4 pl[NL];
 #pragma unroll
   for (int u = 0; u < NL; u++) pl[u] = load16(Prs, ((rsl + RSL * u) * D + 4 * cql) * 4);
-  float xv[(G * D + NT - 1) / NT];
+  float xv[(GR * D + NT - 1) / NT];
 #pragma unroll
-  for (int u = 0; u < (G * D + NT - 1) / NT; u++) {
-    const int e = min(tid + u * NT, G * D - 1);  // clamped: the load needs no branch
-    xv[u] = load_elem<DT>(p.q, q0 * D + e);
+  for (int u = 0; u < (GR * D + NT - 1) / NT; u++) {
+    const int e = min(tid + u * NT, GR * D - 1);  // clamped: the load needs no branch
+    if constexpr (APPEND)
+      xv[u] = e < G * D ? load_elem<DT>(p.q, q0 * D + e)
+                        : load_elem<DT>(p.k_new, head * D + (e - G * D));
+    else
+      xv[u] = load_elem<DT>(p.q, q0 * D + e);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the panel loads
 
@@ -128,7 +149,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
     for (int it = 0; it < NB; it++) {
       const int t = (pass0 + it) * TPP + tl;
-      const uint32_t off = t < S ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
+      const uint32_t off = t < Ss ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
       // a unit with a helper keeps its panel in L2 for the helper's second read
       x[it] = paired ? load16(prs, off) : load16_stream(prs, off);
     }
@@ -138,16 +159,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   issue(xb, NB);
 
 #pragma unroll
-  for (int u = 0; u < (G * D + NT - 1) / NT; u++) {
+  for (int u = 0; u < (GR * D + NT - 1) / NT; u++) {
     const int e = tid + u * NT;
-    if (e < G * D) xq[e / D][e % D] = xv[u];
+    if (e < GR * D) xq[e / D][e % D] = xv[u];
   }
   if (G == 1) select_clear<NT>(ssm);  // the histogram fills while scoring
   __syncthreads();
   {
-    float a[G][4];
+    float a[GR][4];
 #pragma unroll
-    for (int h = 0; h < G; h++)
+    for (int h = 0; h < GR; h++)
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
 #pragma unroll
@@ -155,7 +176,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       float f[4];
       unpack16<F32>(pl[u], f);
 #pragma unroll
-      for (int h = 0; h < G; h++) {
+      for (int h = 0; h < GR; h++) {
         const float x = xq[h][rsl + RSL * u];
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
@@ -165,21 +186,26 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
     for (int o = NQL; o < 64; o <<= 1)
 #pragma unroll
-      for (int h = 0; h < G; h++)
+      for (int h = 0; h < GR; h++)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], o, 64);
     if (lane < NQL)
 #pragma unroll
-      for (int h = 0; h < G; h++)
+      for (int h = 0; h < GR; h++)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) qpart[wave][h][4 * cql + cc] = a[h][cc];
   }
   __syncthreads();
-  for (int e = tid; e < G * DP; e += NT) {
+  for (int e = tid; e < GR * DP; e += NT) {
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; w++) s += qpart[w][e / DP][e % DP];
-    qs[e / DP][e % DP] = s;
+    if (!APPEND || e < G * DP) {
+      qs[e / DP][e % DP] = s;
+    } else {  // panel coordinate of the new key: stored, and kept as stored
+      store_elem<DT>(p.kcache, head * sh.kl.head_elems + (size_t)(S - 1) * DP + e % DP, s);
+      kn[e % DP] = stored_value<DT>(s);
+    }
   }
   __syncthreads();
 
@@ -199,6 +225,28 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       hi[h] = -INFINITY;
 #pragma unroll
       for (int e = 0; e < E; e++) qv[h][e] = qs[h][c * E + e];  // c*E < DP == d
+    }
+    if constexpr (APPEND) {
+      // score of the new token from its stored panel coordinates, summed as
+      // the stream sums a row: lane (h, cl) of wave 0 forms the partial over
+      // coordinates [cl*E, cl*E + E), group_sum adds the LPT partials pairwise
+      // (the reduce-scatter of the single-head stream adds the same pairs)
+      if (wave == 0) {
+        const int h = min(lane / LPT, G - 1), cl = lane % LPT;
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) a = fmaf(qs[h][cl * E + e], kn[cl * E + e], a);
+        a = group_sum<LPT>(a);
+        if (lane < G * LPT && cl == 0) {
+          sc[h * S + S - 1] = a;
+#pragma unroll
+          for (int hh = 0; hh < G; hh++)
+            if (hh == h) {
+              lo[hh] = fminf(lo[hh], a);
+              hi[hh] = fmaxf(hi[hh], a);
+            }
+        }
+      }
     }
     auto consume = [&](const u32x4 (&x)[NB], int pass0, bool hist) {
       if constexpr (G == 1 && LPT == 4 && NB % 4 == 0) {
@@ -223,7 +271,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
           const float u1 = (b0 ? a[g0 + 3] : a[g0 + 2]) + dpp_f<0xB1>(b0 ? a[g0 + 2] : a[g0 + 3]);
           const float r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
           const int t = (pass0 + g0 + c) * TPP + tl;
-          if (t < S) {
+          if (t < Ss) {
             lo[0] = fminf(lo[0], r);
             hi[0] = fmaxf(hi[0], r);
             sc[t] = r;
@@ -243,7 +291,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
           for (int e = 0; e < E; e++) a = fmaf(qv[h][e], f[e], a);
           a = group_sum<LPT>(a);
-          if (t < S) {
+          if (t < Ss) {
             lo[h] = fminf(lo[h], a);
             hi[h] = fmaxf(hi[h], a);
             if (c == (h % LPT)) {
@@ -273,6 +321,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       bscale = bin_scale(blo, bhi);
       for (int t = tid; t < min(S, NB * TPP); t += NT)
         atomicAdd(&ssm.hist[lin_bin(sc[t], blo, bscale)], 1u);
+      if (APPEND && tid == 0 && S - 1 >= NB * TPP)  // the new token, past the first batch
+        atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
     }
     if (2 * NB < n_pass) issue(xa, 2 * NB);
     consume(xb, NB, true);
@@ -305,6 +355,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
 #pragma unroll
   for (int u = 0; u < NR; u++)
     pr[u] = load16(Prs, cqr < NQR ? ((rsr + RSR * u) * D + DP + 4 * cqr) * 4 : kOutOfRange);
+  // the new value row, copied as raw elements (stored with the rest of the key row)
+  using Raw = typename std::conditional<Elem<DT>::kBytes == 4, unsigned, unsigned short>::type;
+  Raw vraw = 0;
+  if constexpr (APPEND) vraw = static_cast<const Raw*>(p.v_new)[head * D + min(tid, D - 1)];
   __syncthreads();
 
   // ---- 2. top-k of each head's scores, from LDS
@@ -314,9 +368,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   constexpr bool kStreamRows = G == 1;
   const bool stream_rows = kStreamRows && k <= kBins / NW;
   auto rotate_rest = [&]() {  // qpart[w][h][DP:D] from the P loads in flight
-    float a[G][4];
+    float a[GR][4];
 #pragma unroll
-    for (int h = 0; h < G; h++)
+    for (int h = 0; h < GR; h++)
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
 #pragma unroll
@@ -324,29 +378,39 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       float f[4];
       unpack16<F32>(pr[u], f);
 #pragma unroll
-      for (int h = 0; h < G; h++) {
+      for (int h = 0; h < GR; h++) {
         const float x = xq[h][rsr + RSR * u];
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; h++)
+    for (int h = 0; h < GR; h++)
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], 32, 64);
     if (lane < 32 && cqr < NQR)
 #pragma unroll
-      for (int h = 0; h < G; h++)
+      for (int h = 0; h < GR; h++)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) qpart[wave][h][DP + 4 * cqr + cc] = a[h][cc];
   };
   auto reduce_rest = [&]() {  // qs[h][DP:D] = sum over the waves of qpart
-    for (int e = tid; e < G * (D - DP); e += NT) {
+    for (int e = tid; e < GR * (D - DP); e += NT) {
       const int h = e / (D - DP), j = DP + e % (D - DP);
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; w++) s += qpart[w][h][j];
-      qs[h][j] = s;
+      if (!APPEND || h < G)
+        qs[h][j] = s;
+      else  // the rest of the new key's row
+        store_elem<DT>(p.kcache, head * sh.kl.head_elems + sh.kl.rest_off +
+                                     (size_t)(S - 1) * (D - DP) + (j - DP), s);
+    }
+    if constexpr (APPEND) {
+      if (tid < D) static_cast<Raw*>(p.vcache)[(head * sh.S_cap + (size_t)(S - 1)) * D + tid] = vraw;
+      // the attention's gathers may read row S-1: every store of this wave
+      // (key row, value row) is complete before the barrier that follows
+      wait_stores();
     }
   };
   if (stream_rows) {
@@ -435,21 +499,27 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   write_idx();
 }
 
-template <int DT, int D, int LPT, int NT>
+template <int DT, int D, int LPT, int NT, bool APPEND>
 hipError_t launch_nt(const FusedParams& p, size_t dyn, hipStream_t st) {
   const dim3 grid((unsigned)(p.n_units + p.n_help));
   switch (p.sh.g) {
-    case 1: fused_kernel<DT, D, LPT, 1, NT><<<grid, NT, dyn, st>>>(p); break;
-    case 2: fused_kernel<DT, D, LPT, 2, NT><<<grid, NT, dyn, st>>>(p); break;
-    default: fused_kernel<DT, D, LPT, 4, NT><<<grid, NT, dyn, st>>>(p); break;
+    case 1: fused_kernel<DT, D, LPT, 1, NT, APPEND><<<grid, NT, dyn, st>>>(p); break;
+    case 2: fused_kernel<DT, D, LPT, 2, NT, APPEND><<<grid, NT, dyn, st>>>(p); break;
+    default: fused_kernel<DT, D, LPT, 4, NT, APPEND><<<grid, NT, dyn, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
+template <int DT, int D, int LPT, int NT>
+hipError_t launch_append(const FusedParams& p, size_t dyn, hipStream_t st) {
+  return p.k_new ? launch_nt<DT, D, LPT, NT, true>(p, dyn, st)
+                 : launch_nt<DT, D, LPT, NT, false>(p, dyn, st);
+}
+
 template <int DT, int D, int LPT>
 hipError_t launch_lpt(const FusedParams& p, size_t dyn, hipStream_t st) {
-  return p.threads == 512 ? launch_nt<DT, D, LPT, 512>(p, dyn, st)
-                          : launch_nt<DT, D, LPT, 256>(p, dyn, st);
+  return p.threads == 512 ? launch_append<DT, D, LPT, 512>(p, dyn, st)
+                          : launch_append<DT, D, LPT, 256>(p, dyn, st);
 }
 
 template <int DT>

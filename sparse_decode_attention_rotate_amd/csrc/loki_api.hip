@@ -193,9 +193,11 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   const bool split = (d == sh.dp);
   float* sel = split ? reinterpret_cast<float*>(ws + w.sel) : nullptr;
 
-  if (!append && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
+  if (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
     FusedParams fp{};
     fp.q = q;
+    fp.k_new = append ? k_new : nullptr;
+    fp.v_new = append ? v_new : nullptr;
     fp.kcache = kcache;
     fp.vcache = vcache;
     fp.P = P;
@@ -321,8 +323,8 @@ int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_l
   if (!one_launch) return fail(LOKI_EINVAL, "one_launch is NULL");
   if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
-  *one_launch = (!append && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) &&
-                 fused_supported(sh, d, k)) ? 1 : 0;
+  (void)append;  // the one-launch kernel appends too
+  *one_launch = (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) ? 1 : 0;
   return LOKI_OK;
 }
 

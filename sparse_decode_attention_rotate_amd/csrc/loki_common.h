@@ -73,16 +73,24 @@ template <> __device__ __forceinline__ void store_elem<F32>(void* base, size_t i
 template <> __device__ __forceinline__ void store_elem<F16>(void* base, size_t i, float x) {
   static_cast<_Float16*>(base)[i] = (_Float16)x;
 }
-template <> __device__ __forceinline__ void store_elem<BF16>(void* base, size_t i, float x) {
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
   unsigned u = __float_as_uint(x);
-  unsigned short r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) {
-    r = (unsigned short)((u >> 16) | 0x40u);  // quiet NaN
-  } else {
-    u += 0x7fffu + ((u >> 16) & 1u);            // round half to even on bit 16
-    r = (unsigned short)(u >> 16);
-  }
-  static_cast<unsigned short*>(base)[i] = r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);  // round half to even on bit 16
+  return (unsigned short)(u >> 16);
+}
+template <> __device__ __forceinline__ void store_elem<BF16>(void* base, size_t i, float x) {
+  static_cast<unsigned short*>(base)[i] = bf16_bits(x);
+}
+
+// The value store_elem<DT> keeps, as fp32.
+template <int DT> __device__ __forceinline__ float stored_value(float x);
+template <> __device__ __forceinline__ float stored_value<F32>(float x) { return x; }
+template <> __device__ __forceinline__ float stored_value<F16>(float x) {
+  return (float)(_Float16)x;
+}
+template <> __device__ __forceinline__ float stored_value<BF16>(float x) {
+  return __uint_as_float((unsigned)bf16_bits(x) << 16);
 }
 
 // Raw element copy (no conversion), for moving stored rows.

@@ -61,8 +61,10 @@ struct AttendParams {
 
 struct FusedParams {
   const void* q;        // [B,Hq,D]
-  const void* kcache;
-  const void* vcache;
+  const void* k_new;    // [B,Hkv,D] nullable: appended as token S-1 when set
+  const void* v_new;    // [B,Hkv,D]
+  void* kcache;         // written only at row S-1, when appending
+  void* vcache;
   const float* P;       // [Hkv,D,D]
   float* out;           // [B,Hq,D]
   int32_t* idx_out;     // [B,Hq,k] nullable

@@ -95,29 +95,33 @@ def test_append_row(L, dtype, dp):
     L.append(dev["k_new"], dev["v_new"], dev["P"], dev["kcache"], dev["v"], pos, desc)
     rows = L.unpack_kcache(dev["kcache"], 64, desc.with_seq_len(64))
     torch.cuda.synchronize()
-    got = H.to_host(rows, dtype)
+    _check_appended(dtype, x, H.to_host(rows, dtype), H.to_host(dev["v"], dtype), pos)
+
+
+def _check_appended(dtype, x, got, v_got, pos):
+    """Row pos of the K cache (unpacked rows `got`) and of the V cache
+    `v_got` against the oracle's append; every other row unchanged."""
     kr, vr = oracle.append_rows(x["k_new"], x["v_new"], x["P"], dtype)
     g = W.from_storage(got[:, :, pos], dtype)
     r = W.from_storage(kr, dtype)
     frac_exact = np.mean(g == r)
     H.log(f"  appended elements equal to the oracle's rounding: {frac_exact:.5f}")
+    D = g.shape[-1]
+    kn = W.from_storage(x["k_new"], dtype)
+    mag = np.einsum("bhi,hij->bhj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
     if dtype == "f32":
         # the stored value is the fp32 product itself: fp32 dot-product error bound
-        kn = W.from_storage(x["k_new"], dtype)
-        mag = np.einsum("bhi,hij->bhj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
-        assert np.all(np.abs(g - r) <= 2 * 128 * 2.0 ** -24 * mag)
+        assert np.all(np.abs(g - r) <= 2 * D * 2.0 ** -24 * mag)
     else:
         # fp32 product rounded once to f16 / bf16: one unit in the last place
         # plus the fp32 dot-product error (which matters only under cancellation)
-        kn = W.from_storage(x["k_new"], dtype)
-        mag = np.einsum("bhi,hij->bhj", np.abs(kn), np.abs(x["P"].astype(np.float64)))
-        assert np.all(np.abs(g - r) <= _ulp(r, dtype) + 2 * 128 * 2.0 ** -24 * mag)
+        assert np.all(np.abs(g - r) <= _ulp(r, dtype) + 2 * D * 2.0 ** -24 * mag)
         assert frac_exact > 0.99
-    assert np.array_equal(H.to_host(dev["v"], dtype)[:, :, pos], vr)
-    # other rows untouched
-    keep = np.ones(64, bool)
+    assert np.array_equal(v_got[:, :, pos], vr)
+    keep = np.ones(got.shape[2], bool)
     keep[pos] = False
     assert np.array_equal(got[:, :, keep], x["krot"][:, :, keep])
+    assert np.array_equal(v_got[:, :, keep], x["v"][:, :, keep])
 
 
 # ----------------------------------------------------------------- prefill
@@ -450,18 +454,74 @@ def test_launch_plan(L):
         assert not L.decode_plan(desc.with_flags(L.FLAG_SEPARATE_KERNELS), wl.d, wl.k)
     wl = _small("f16", S=3000, k=300)
     assert not L.decode_plan(H.make_desc(wl, 32), 20, 300)      # d != dp
-    assert not L.decode_plan(H.make_desc(wl, 32), 32, 300, True)  # append
+    assert L.decode_plan(H.make_desc(wl, 32), 32, 300, True)    # append: the same kernel
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_decode_append_end_to_end(L, dtype):
-    wl = _small(dtype, S=2600, S_cap=3000, k=333, append=True, heavy_frac=0.02)
-    H.log(f"decode_append {dtype}")
+def _decode_append_check(L, wl, separate, selected=False):
     x = W.generate(wl)
-    dev = H.upload(wl, x)
-    out, idx = H.run_decode(wl, dev)
+    P = x["P"].astype(np.float64)
+    qf = W.from_storage(x["q"], wl.dtype)[:, ::wl.g]          # first query of each group
+    qr = np.einsum("bhi,hij->bhj", qf, P)
+    if selected:
+        # the new key along that query: its score is the largest of the row,
+        # so the attention gathers the appended row
+        x["k_new"] = W.to_storage(2.0 * qf, wl.dtype)
+    # stale contents in row S-1 of both caches (a key scoring far below every
+    # other token, large values): reading the row before the append shows in
+    # the selection or the output
+    xs = dict(x, krot=x["krot"].copy(), v=x["v"].copy())
+    xs["krot"][:, :, wl.S - 1] = W.to_storage(-8.0 * np.sign(qr), wl.dtype)
+    xs["v"][:, :, wl.S - 1] = W.to_storage(np.full((wl.B, wl.Hkv, wl.D), 50.0), wl.dtype)
+    dev = H.upload(wl, xs)
+    out, idx = H.run_decode(wl, dev, separate=separate)
     res = H.full_parity(wl, x, out, idx)
     H.log(f"  {res}")
+    rows = L.unpack_kcache(dev["kcache"], wl.capacity, dev["desc"].with_seq_len(wl.capacity))
+    torch.cuda.synchronize()
+    _check_appended(wl.dtype, x, H.to_host(rows, wl.dtype), H.to_host(dev["v"], wl.dtype),
+                    wl.S - 1)
+
+
+@pytest.mark.parametrize("separate", [False, True], ids=["default", "separate"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_decode_append_end_to_end(L, dtype, separate):
+    wl = _small(dtype, S=2600, S_cap=3000, k=333, append=True, heavy_frac=0.02)
+    H.log(f"decode_append {dtype} separate={separate}")
+    _decode_append_check(L, wl, separate)
+
+
+# One-launch appends: the new token's score enters the selection in the first
+# panel batch or after it (512 threads: 1024 tokens per batch, 256 threads:
+# 512), with helper workgroups, through the large-k selection, in GQA groups,
+# and at the smallest sizes.
+APPEND_FUSED = {
+    "g1-512-past-first-batch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1025, S_cap=1100, k=100),
+    "g1-512-in-first-batch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1024, S_cap=1100, k=100),
+    "g1-512-selected": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1500, S_cap=1500, k=100,
+                            selected=True),
+    "g1-256-helpers": dict(dtype="bf16", B=8, Hq=40, Hkv=40, S=513, S_cap=600, k=300),
+    "g1-256-helpers-selected": dict(dtype="bf16", B=8, Hq=40, Hkv=40, S=900, S_cap=900, k=300,
+                                    selected=True),
+    "g1-256-large-k": dict(dtype="f16", B=8, Hq=40, Hkv=40, S=2000, S_cap=2048, k=600,
+                           selected=True),
+    "g2-f32": dict(dtype="f32", B=2, Hq=8, Hkv=4, S=700, S_cap=800, k=64, selected=True),
+    "g4-bf16": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, S_cap=1800, k=200),
+    "g4-bf16-selected": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, S_cap=1800, k=200,
+                             selected=True),
+    "S1": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1, S_cap=8, k=1),
+    "k-eq-S": dict(dtype="f16", B=2, Hq=8, Hkv=4, S=300, S_cap=320, k=300),
+}
+
+
+@pytest.mark.parametrize("case", list(APPEND_FUSED), ids=list(APPEND_FUSED))
+def test_decode_append_one_launch(L, case):
+    kw = dict(APPEND_FUSED[case])
+    selected = kw.pop("selected", False)
+    wl = _small(append=True, **kw)
+    desc = H.make_desc(wl, 32)
+    assert L.decode_plan(desc, wl.d, wl.k, True), f"{case} is meant to take the one-launch kernel"
+    H.log(f"decode_append one launch {case}: {W.describe(wl)}")
+    _decode_append_check(L, wl, separate=False, selected=selected)
 
 
 def test_softmax_scale_argument(L):
