@@ -135,15 +135,15 @@ def main():
                 calls.append((loki.lib.loki_decode_append,
                               (vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
                                vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d,
-                               wl.k, vp(out.data_ptr()), None, ctypes.byref(cd),
+                               wl.k, vp(out.data_ptr()), None, None, ctypes.byref(cd),
                                vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))))
             else:
                 # the step of the method: loki_decode(q, Kcache_rot, V, P, d, k, out);
-                # the optional index output is not requested
+                # the optional index and score outputs are not requested
                 calls.append((loki.lib.loki_decode,
                               (vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
                                vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()),
-                               None, ctypes.byref(cd), vp(ws.data_ptr()),
+                               None, None, ctypes.byref(cd), vp(ws.data_ptr()),
                                ws.numel(), vp(stream.cuda_stream))))
         return cd, calls
 
@@ -213,8 +213,8 @@ def main():
         if rc != 0:
             raise RuntimeError(f"{loki.strerror(rc)} {loki.last_error()}")
 
-    lib.loki_decode(q_, kcs[0], vcs[0], P_, wl.d, wl.k, out_, idx_, ctypes.byref(cdesc_sep),
-                    ws_, ws.numel(), st)
+    lib.loki_decode(q_, kcs[0], vcs[0], P_, wl.d, wl.k, out_, idx_, None,
+                    ctypes.byref(cdesc_sep), ws_, ws.numel(), st)
     chk(lib.loki_rotate_query(q_, P_, qr_, cd, st))
     chk(lib.loki_score(qr_, kcs[0], wl.d, sc_, cd, st))
     chk(lib.loki_topk(sc_, wl.k, idx_, sel_, cd, st))
@@ -259,10 +259,11 @@ def main():
         ws_x = loki.empty_workspace(desc_x, wl.D, wl.k)
         cdx = desc_x.c()
         kcx_, wsx_ = vp(kc_x.data_ptr()), vp(ws_x.data_ptr())
-        chk(lib.loki_decode(q_, kcx_, vcs[0], P_, wl.D, wl.k, out_, None, ctypes.byref(cdx), wsx_,
-                            ws_x.numel(), st))
+        chk(lib.loki_decode(q_, kcx_, vcs[0], P_, wl.D, wl.k, out_, None, None, ctypes.byref(cdx),
+                            wsx_, ws_x.numel(), st))
         exact_us = timed(lambda i: lib.loki_decode(q_, kcx_, vcs[i % len(vcs)], P_, wl.D, wl.k, out_,
-                                                   None, ctypes.byref(cdx), wsx_, ws_x.numel(), st))
+                                                   None, None, ctypes.byref(cdx), wsx_, ws_x.numel(),
+                                                   st))
         exact_bytes = es_ * (wl.B * wl.Hkv * wl.S * wl.D + wl.B * wl.Hq * wl.k * wl.D)
         exact = {"us_per_step": round(exact_us, 2), "bytes_per_step": exact_bytes,
                  "GBps": round(exact_bytes / (exact_us * 1e-6) / 1e9, 1),
@@ -325,7 +326,7 @@ def main():
 
         def append_call(i, cd_):
             chk(lib.loki_decode_append(q_, kn_, vn_, kcs[i % len(kcs)], vcs[i % len(vcs)], P_,
-                                       wl.d, wl.k, out_, None, cd_, ws_, ws.numel(), st))
+                                       wl.d, wl.k, out_, None, None, cd_, ws_, ws.numel(), st))
 
         # the decode step timed again just before, under the same conditions
         dec_us = timed(lambda i: step(i))

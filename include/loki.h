@@ -52,7 +52,7 @@
  *            direction (descending variance), so k_rot = k . P.  Query head h
  *            uses P[h / (Hq/Hkv)].
  *   qr       [B, Hq, D] fp32, scores [B, Hq, S] fp32, idx [B, Hq, k] int32,
- *   out      [B, Hq, D] fp32.
+ *   out      [B, Hq, D] in loki_desc.out_dtype (fp32 by default).
  */
 #ifndef LOKI_H
 #define LOKI_H
@@ -88,6 +88,9 @@ typedef struct {
   int32_t dtype;        /* loki_dtype of q, K cache, V cache, k_new, v_new */
   float softmax_scale;  /* <= 0 selects 1/sqrt(D) */
   uint32_t flags;       /* LOKI_FLAG_* bits, 0 by default */
+  int32_t out_dtype;    /* loki_dtype of every attention output `out`: LOKI_F32
+                           (0, the default) or LOKI_F16 / LOKI_BF16, the fp32
+                           result rounded to nearest-even once at the store */
 } loki_desc;
 
 /* loki_desc.flags: run a decode step as separate launches (query rotation,
@@ -196,18 +199,23 @@ int loki_topk(const float* scores, int k, int32_t* idx, float* sel_out, const lo
  * Needs loki_workspace_bytes(desc, D, k) bytes of workspace.
  */
 int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
-                const float* sel_scores, int k, float* out, const loki_desc* desc,
+                const float* sel_scores, int k, void* out, const loki_desc* desc,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One full Loki decode step [A], [T], [F1]: rotate q, score all S tokens
  * with the leading d coordinates, select the top k per (b, h), exact softmax
- * attention over them.  1 <= d <= D, 1 <= k <= S.  idx_out (nullable)
- * receives the selected sets [B, Hq, k] in ascending order.
+ * attention over them.  1 <= d <= D, 1 <= k <= S.  out [B, Hq, D] in
+ * desc->out_dtype.  idx_out (nullable) receives the selected sets
+ * [B, Hq, k] in ascending order.  scores_out (nullable, [B, Hq, S] fp32,
+ * 16-byte aligned) receives the low-dimensional scores of every token, the
+ * values the selection ranked; a call with scores_out runs as separate
+ * launches (the one-launch kernel keeps its scores on chip), whatever
+ * loki_decode_plan reports.
  */
 int loki_decode(const void* q, const void* kcache, const void* vcache, const float* P, int d,
-                int k, float* out, int32_t* idx_out, const loki_desc* desc, void* workspace,
-                size_t workspace_bytes, void* stream);
+                int k, void* out, int32_t* idx_out, float* scores_out, const loki_desc* desc,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Append then decode [C], [F1]: appends (k_new, v_new) at row pos = S-1 as
@@ -221,9 +229,9 @@ int loki_decode(const void* q, const void* kcache, const void* vcache, const flo
  * order before the rounding).
  */
 int loki_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
-                       void* vcache, const float* P, int d, int k, float* out,
-                       int32_t* idx_out, const loki_desc* desc, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       void* vcache, const float* P, int d, int k, void* out,
+                       int32_t* idx_out, float* scores_out, const loki_desc* desc,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Dense decode attention over all S cached tokens, the baseline the pages
@@ -231,12 +239,12 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
  * over vanilla attention): qr = q . P[kv], z_t = scale * qr . krot_t over all
  * D coordinates of every token t < S, out = softmax(z) . V.  Because P is
  * orthonormal, qr . krot_t = q . k_t: this is ordinary full attention, read
- * from the same rotated cache.  out [B, Hq, D] fp32.  Split over chunks of
+ * from the same rotated cache.  out [B, Hq, D] in desc->out_dtype.  Split over chunks of
  * the sequence; partial softmax states are merged by a second launch.
  * Needs loki_workspace_bytes(desc, D, seq_len) bytes of workspace.
  */
 int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
-                        float* out, const loki_desc* desc, void* workspace,
+                        void* out, const loki_desc* desc, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /*
@@ -245,11 +253,11 @@ int loki_full_attention(const void* q, const void* kcache, const void* vcache, c
  * for every token t < S (no selection), out = softmax(z) . V over all S
  * tokens.  1 <= d <= D; d = D gives loki_full_attention's result.  Reads the
  * leading d coordinates of each cached key (the panel when d <= panel_dim)
- * and every V row.  out [B, Hq, D] fp32.  Needs
+ * and every V row.  out [B, Hq, D] in desc->out_dtype.  Needs
  * loki_workspace_bytes(desc, D, seq_len) bytes of workspace.
  */
 int loki_pca_attention(const void* q, const void* kcache, const void* vcache, const float* P,
-                       int d, float* out, const loki_desc* desc, void* workspace,
+                       int d, void* out, const loki_desc* desc, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /*

@@ -48,7 +48,8 @@ class _CDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("seq_len", ctypes.c_int32), ("seq_capacity", ctypes.c_int32),
                 ("panel_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+                ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("out_dtype", ctypes.c_int32)]
 
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -65,9 +66,9 @@ _SIG = {
     "loki_score": ([_vp, _vp, _i, _vp, _D, _vp], _i),
     "loki_topk": ([_vp, _i, _vp, _vp, _D, _vp], _i),
     "loki_attend": ([_vp, _vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
-    "loki_decode": ([_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _D, _vp, _sz, _vp], _i),
-    "loki_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _D, _vp, _sz, _vp],
-                           _i),
+    "loki_decode": ([_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
+    "loki_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _D, _vp, _sz,
+                            _vp], _i),
     "loki_decode_plan": ([_D, _i, _i, _i, ctypes.POINTER(_i)], _i),
     "loki_full_attention": ([_vp, _vp, _vp, _vp, _vp, _D, _vp, _sz, _vp], _i),
     "loki_pca_attention": ([_vp, _vp, _vp, _vp, _i, _vp, _D, _vp, _sz, _vp], _i),
@@ -101,14 +102,18 @@ class Desc:
     dtype: int
     softmax_scale: float = 0.0
     flags: int = 0
+    out_dtype: int = F32
 
     def c(self) -> _CDesc:
         return _CDesc(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.seq_len,
                       self.seq_capacity, self.panel_dim, self.dtype, self.softmax_scale,
-                      self.flags)
+                      self.flags, self.out_dtype)
 
     def with_flags(self, flags: int) -> "Desc":
         return dataclasses.replace(self, flags=flags)
+
+    def with_out_dtype(self, out_dtype: int) -> "Desc":
+        return dataclasses.replace(self, out_dtype=out_dtype)
 
     def with_seq_len(self, s: int) -> "Desc":
         return dataclasses.replace(self, seq_len=s)
@@ -116,6 +121,10 @@ class Desc:
     @property
     def torch_dtype(self) -> torch.dtype:
         return TORCH_DTYPE[self.dtype]
+
+    @property
+    def torch_out_dtype(self) -> torch.dtype:
+        return TORCH_DTYPE[self.out_dtype]
 
 
 def _check(rc: int, where: str) -> None:
@@ -131,6 +140,15 @@ def _ptr(t: Optional[torch.Tensor]):
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(desc: "Desc", out, device):
+    """The attention output [B, Hq, D] in desc's output dtype (allocated if None)."""
+    shp = (desc.batch, desc.n_q_heads, desc.head_dim)
+    if out is None:
+        return torch.empty(shp, dtype=desc.torch_out_dtype, device=device)
+    _expect(out, shp, desc.torch_out_dtype, "out")
+    return out
 
 
 def _stream(stream=None):
@@ -257,9 +275,7 @@ def attend(qr, kcache, vcache, idx, desc: Desc, out=None, workspace=None, sel_sc
     panel_dim coordinates) only the remaining key coordinates are read."""
     k = idx.shape[-1]
     _expect(idx, (desc.batch, desc.n_q_heads, k), torch.int32, "idx")
-    if out is None:
-        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
-                          device=qr.device)
+    out = _out(desc, out, qr.device)
     if workspace is None:
         workspace = empty_workspace(desc, desc.head_dim, k, qr.device)
     _check(_lib.loki_attend(_ptr(qr), _ptr(kcache), _ptr(vcache), _ptr(idx), _ptr(sel_scores), k,
@@ -269,44 +285,53 @@ def attend(qr, kcache, vcache, idx, desc: Desc, out=None, workspace=None, sel_sc
     return out
 
 
+def _check_decode_outputs(desc: Desc, k: int, idx_out, scores_out):
+    if idx_out is not None:
+        _expect(idx_out, (desc.batch, desc.n_q_heads, k), torch.int32, "idx_out")
+    if scores_out is not None:
+        _expect(scores_out, (desc.batch, desc.n_q_heads, desc.seq_len), torch.float32,
+                "scores_out")
+
+
 def decode(q, kcache, vcache, P, d: int, k: int, desc: Desc, out=None, idx_out=None,
-           workspace=None, stream=None):
-    """One Loki decode step; returns out [B, Hq, D] fp32 (and fills idx_out if given)."""
+           workspace=None, stream=None, scores_out=None):
+    """One Loki decode step; returns out [B, Hq, D] in desc's output dtype (and
+    fills idx_out [B, Hq, k] and scores_out [B, Hq, S] fp32 if given)."""
     _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
-    if out is None:
-        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
-                          device=q.device)
+    _check_decode_outputs(desc, k, idx_out, scores_out)
+    out = _out(desc, out, q.device)
     if workspace is None:
         workspace = empty_workspace(desc, d, k, q.device)
     _check(_lib.loki_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), d, k, _ptr(out),
-                            _ptr(idx_out), ctypes.byref(desc.c()), _ptr(workspace),
-                            workspace.numel(), _stream(stream)), "loki_decode")
+                            _ptr(idx_out), _ptr(scores_out), ctypes.byref(desc.c()),
+                            _ptr(workspace), workspace.numel(), _stream(stream)), "loki_decode")
     return out
 
 
 def decode_append(q, k_new, v_new, kcache, vcache, P, d: int, k: int, desc: Desc, out=None,
-                  idx_out=None, workspace=None, stream=None):
+                  idx_out=None, workspace=None, stream=None, scores_out=None):
     """Append (k_new, v_new) at row seq_len-1, then one decode step over seq_len tokens."""
     _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
-    if out is None:
-        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
-                          device=q.device)
+    shp = (desc.batch, desc.n_kv_heads, desc.head_dim)
+    _expect(k_new, shp, desc.torch_dtype, "k_new")
+    _expect(v_new, shp, desc.torch_dtype, "v_new")
+    _check_decode_outputs(desc, k, idx_out, scores_out)
+    out = _out(desc, out, q.device)
     if workspace is None:
         workspace = empty_workspace(desc, d, k, q.device)
     _check(_lib.loki_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kcache), _ptr(vcache),
-                                   _ptr(P), d, k, _ptr(out), _ptr(idx_out), ctypes.byref(desc.c()),
-                                   _ptr(workspace), workspace.numel(), _stream(stream)),
+                                   _ptr(P), d, k, _ptr(out), _ptr(idx_out), _ptr(scores_out),
+                                   ctypes.byref(desc.c()), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)),
            "loki_decode_append")
     return out
 
 
 def full_attention(q, kcache, vcache, P, desc: Desc, out=None, workspace=None, stream=None):
     """Dense decode attention over all seq_len cached tokens (the baseline of
-    the Loki step); returns out [B, Hq, D] fp32."""
+    the Loki step); returns out [B, Hq, D] in desc's output dtype."""
     _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
-    if out is None:
-        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
-                          device=q.device)
+    out = _out(desc, out, q.device)
     if workspace is None:
         workspace = empty_workspace(desc, desc.head_dim, desc.seq_len, q.device)
     _check(_lib.loki_full_attention(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), _ptr(out),
@@ -319,11 +344,9 @@ def pca_attention(q, kcache, vcache, P, d: int, desc: Desc, out=None, workspace=
                   stream=None):
     """PCAAttn: softmax over all seq_len tokens of the scaled scores from the
     leading d rotated coordinates, weighted sum of all V rows; returns out
-    [B, Hq, D] fp32."""
+    [B, Hq, D] in desc's output dtype."""
     _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
-    if out is None:
-        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
-                          device=q.device)
+    out = _out(desc, out, q.device)
     if workspace is None:
         workspace = empty_workspace(desc, desc.head_dim, desc.seq_len, q.device)
     _check(_lib.loki_pca_attention(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), d, _ptr(out),

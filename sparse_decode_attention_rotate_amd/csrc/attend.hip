@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
       p.qr + bh * D, p.scale_log2, sidx, slow, nr, p.kcache, p.vcache, head, sh, sm, M, L, A, p.d);
   if (tid < D) {
     if (p.nsplit == 1) {
-      p.out[bh * D + tid] = A / L;
+      store_out(p.out, bh * D + tid, A / L, sh.odt);
     } else {
       float* part = p.part + (bh * p.nsplit + split) * (size_t)(D + 2);
       part[2 + tid] = A;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
     L = fmaf(ps[1], w, L);
     a = fmaf(ps[2 + threadIdx.x], w, a);
   }
-  p.out[bh * D + threadIdx.x] = a / L;
+  store_out(p.out, bh * D + threadIdx.x, a / L, p.sh.odt);
 }
 
 template <int DT, int D>

@@ -483,8 +483,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       const float oM = ld_coherent(other), oL = ld_coherent(other + 1);
       const float oA = ld_coherent(other + 2 + tid);
       // always the owner's half first: the result does not depend on which merges
-      p.out[head * D + tid] = helper ? combine_partials(oM, oL, oA, M, L, A)
-                                     : combine_partials(M, L, A, oM, oL, oA);
+      store_out(p.out, head * D + tid,
+                helper ? combine_partials(oM, oL, oA, M, L, A)
+                       : combine_partials(M, L, A, oM, oL, oA),
+                sh.odt);
     }
     write_idx();
     return;
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     float M, L, A;
     block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, G == 1>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
                                   p.kcache, p.vcache, head, sh, asm_, M, L, A);
-    if (tid < D) p.out[(q0 + h) * D + tid] = A / L;
+    if (tid < D) store_out(p.out, (q0 + h) * D + tid, A / L, sh.odt);
     __syncthreads();  // asm_ is reused by the next head
   }
   write_idx();

@@ -56,6 +56,8 @@ int check_desc(const loki_desc* d, Shape* sh) {
   if (g > 16) return fail(LOKI_EUNSUPPORTED, "query heads per KV head (%d) above 16", g);
   if (d->dtype != LOKI_F32 && d->dtype != LOKI_F16 && d->dtype != LOKI_BF16)
     return fail(LOKI_EINVAL, "dtype %d is not a loki_dtype", d->dtype);
+  if (d->out_dtype != LOKI_F32 && d->out_dtype != LOKI_F16 && d->out_dtype != LOKI_BF16)
+    return fail(LOKI_EINVAL, "out_dtype %d is not a loki_dtype", d->out_dtype);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(LOKI_EUNSUPPORTED, "head_dim %d (built: 64, 128)", d->head_dim);
   if (d->seq_len < 1 || d->seq_capacity < d->seq_len || d->seq_capacity > (1 << 30))
@@ -78,6 +80,7 @@ int check_desc(const loki_desc* d, Shape* sh) {
   sh->S_cap = d->seq_capacity;
   sh->dp = dp;
   sh->dtype = d->dtype;
+  sh->odt = d->out_dtype;
   sh->kl.head_elems = (size_t)d->seq_capacity * d->head_dim;
   sh->kl.rest_off = (size_t)d->seq_capacity * dp;
   sh->kl.dp = dp;
@@ -162,7 +165,7 @@ float scale_log2(const loki_desc* d) {
 }
 
 int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
-                const float* P, int d, int k, float* out, int32_t* idx_out,
+                const float* P, int d, int k, void* out, int32_t* idx_out, float* scores_out,
                 const loki_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
                 bool append) {
   Shape sh;
@@ -179,6 +182,8 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     REQUIRE_PTR(v_new);
   }
   if (idx_out && !aligned16(idx_out)) return fail(LOKI_EINVAL, "idx_out is not 16-byte aligned");
+  if (scores_out && !aligned16(scores_out))
+    return fail(LOKI_EINVAL, "scores_out is not 16-byte aligned");
   if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
   const WsLayout w = ws_layout(sh, k);
@@ -188,12 +193,14 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   float* qr = reinterpret_cast<float*>(ws + w.qr);
-  float* scores = reinterpret_cast<float*>(ws + w.scores);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + w.idx);
   const bool split = (d == sh.dp);
   float* sel = split ? reinterpret_cast<float*>(ws + w.sel) : nullptr;
 
-  if (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
+  // the one-launch kernel keeps the scores on chip: a call that asks for
+  // them takes the separate launches
+  if (!scores_out && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
     FusedParams fp{};
     fp.q = q;
     fp.k_new = append ? k_new : nullptr;
@@ -463,7 +470,7 @@ int loki_topk(const float* scores, int k, int32_t* idx, float* sel_out, const lo
 }
 
 int loki_attend(const float* qr, const void* kcache, const void* vcache, const int32_t* idx,
-                const float* sel_scores, int k, float* out, const loki_desc* desc,
+                const float* sel_scores, int k, void* out, const loki_desc* desc,
                 void* workspace, size_t workspace_bytes, void* stream) {
   Shape sh;
   int rc = check_desc(desc, &sh);
@@ -498,24 +505,25 @@ int loki_attend(const float* qr, const void* kcache, const void* vcache, const i
 }
 
 int loki_decode(const void* q, const void* kcache, const void* vcache, const float* P, int d,
-                int k, float* out, int32_t* idx_out, const loki_desc* desc, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                int k, void* out, int32_t* idx_out, float* scores_out, const loki_desc* desc,
+                void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, nullptr, nullptr, const_cast<void*>(kcache), const_cast<void*>(vcache),
-                     P, d, k, out, idx_out, desc, workspace, workspace_bytes, stream, false);
+                     P, d, k, out, idx_out, scores_out, desc, workspace, workspace_bytes, stream,
+                     false);
 }
 
 int loki_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
-                       void* vcache, const float* P, int d, int k, float* out,
-                       int32_t* idx_out, const loki_desc* desc, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  return decode_impl(q, k_new, v_new, kcache, vcache, P, d, k, out, idx_out, desc, workspace,
-                     workspace_bytes, stream, true);
+                       void* vcache, const float* P, int d, int k, void* out,
+                       int32_t* idx_out, float* scores_out, const loki_desc* desc,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_new, v_new, kcache, vcache, P, d, k, out, idx_out, scores_out, desc,
+                     workspace, workspace_bytes, stream, true);
 }
 
 // Dense (low_dim = 0) or low-dimensional (PCAAttn) attention over all S
 // tokens: query rotation, then the split attention with identity rows.
 static int all_tokens_attention(const void* q, const void* kcache, const void* vcache,
-                                const float* P, int d, int low_dim, float* out,
+                                const float* P, int d, int low_dim, void* out,
                                 const loki_desc* desc, void* workspace, size_t workspace_bytes,
                                 void* stream, const char* what) {
   Shape sh;
@@ -563,7 +571,7 @@ static int all_tokens_attention(const void* q, const void* kcache, const void* v
 }
 
 int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
-                        float* out, const loki_desc* desc, void* workspace,
+                        void* out, const loki_desc* desc, void* workspace,
                         size_t workspace_bytes, void* stream) {
   const int D = desc ? desc->head_dim : 1;
   return all_tokens_attention(q, kcache, vcache, P, D, 0, out, desc, workspace, workspace_bytes,
@@ -571,7 +579,7 @@ int loki_full_attention(const void* q, const void* kcache, const void* vcache, c
 }
 
 int loki_pca_attention(const void* q, const void* kcache, const void* vcache, const float* P,
-                       int d, float* out, const loki_desc* desc, void* workspace,
+                       int d, void* out, const loki_desc* desc, void* workspace,
                        size_t workspace_bytes, void* stream) {
   return all_tokens_attention(q, kcache, vcache, P, d, 1, out, desc, workspace, workspace_bytes,
                               stream, "pca_attention");

@@ -83,6 +83,16 @@ template <> __device__ __forceinline__ void store_elem<BF16>(void* base, size_t 
   static_cast<unsigned short*>(base)[i] = bf16_bits(x);
 }
 
+// An attention output element in the output dtype (uniform across the wave).
+__device__ __forceinline__ void store_out(void* base, size_t i, float x, int odt) {
+  if (odt == F32)
+    store_elem<F32>(base, i, x);
+  else if (odt == F16)
+    store_elem<F16>(base, i, x);
+  else
+    store_elem<BF16>(base, i, x);
+}
+
 // The value store_elem<DT> keeps, as fp32.
 template <int DT> __device__ __forceinline__ float stored_value(float x);
 template <> __device__ __forceinline__ float stored_value<F32>(float x) { return x; }

@@ -11,6 +11,7 @@ namespace loki {
 
 struct Shape {
   int B, Hq, Hkv, g, D, S, S_cap, dp, dtype;
+  int odt;  // dtype of the attention output
   KLayout kl;
 };
 
@@ -51,7 +52,7 @@ struct AttendParams {
   const void* vcache;
   const int32_t* idx;       // [B*Hq, k]; null: row r is token r (k = S, dense attention)
   const float* sel_scores;  // [B*Hq, k] low-dim partial logits (split variant) or null
-  float* out;               // [B,Hq,D] fp32 (written when nsplit == 1 or by combine)
+  void* out;                // [B,Hq,D] in sh.odt (written when nsplit == 1 or by combine)
   float* part;              // [B*Hq, nsplit, D+2] partial (m, l, acc)
   int k, d, nsplit, kc;
   int low_dim;              // logits from the leading d coordinates only (PCAAttn)
@@ -66,7 +67,7 @@ struct FusedParams {
   void* kcache;         // written only at row S-1, when appending
   void* vcache;
   const float* P;       // [Hkv,D,D]
-  float* out;           // [B,Hq,D]
+  void* out;            // [B,Hq,D] in sh.odt
   int32_t* idx_out;     // [B,Hq,k] nullable
   int k;
   float scale_log2;

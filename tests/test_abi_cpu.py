@@ -67,7 +67,7 @@ def _desc(L, **kw):
     (dict(head_dim=96), -2), (dict(head_dim=256), -2), (dict(dtype=7), -1),
     (dict(seq_len=0), -1), (dict(seq_capacity=50), -1), (dict(panel_dim=24), -1),
     (dict(panel_dim=4), -1), (dict(panel_dim=256), -1),
-    (dict(n_q_heads=34, n_kv_heads=2), -2),
+    (dict(n_q_heads=34, n_kv_heads=2), -2), (dict(out_dtype=3), -1), (dict(out_dtype=-1), -1),
 ])
 def test_desc_validation(L, kw, code):
     n = ctypes.c_size_t()
@@ -98,20 +98,23 @@ def test_decode_rejects_bad_arguments_before_launch(L):
     odd = ctypes.c_void_p(0x10004)
     f = L.lib.loki_decode
     # null pointers
-    assert f(None, fake, fake, fake, 32, 10, fake, None, cd, fake, 1 << 30, None) == -1
-    assert f(fake, fake, fake, fake, 32, 10, None, None, cd, fake, 1 << 30, None) == -1
+    assert f(None, fake, fake, fake, 32, 10, fake, None, None, cd, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 32, 10, None, None, None, cd, fake, 1 << 30, None) == -1
     # misaligned
-    assert f(odd, fake, fake, fake, 32, 10, fake, None, cd, fake, 1 << 30, None) == -1
+    assert f(odd, fake, fake, fake, 32, 10, fake, None, None, cd, fake, 1 << 30, None) == -1
     assert "aligned" in L.last_error()
     # d, k domain
-    assert f(fake, fake, fake, fake, 0, 10, fake, None, cd, fake, 1 << 30, None) == -1
-    assert f(fake, fake, fake, fake, 129, 10, fake, None, cd, fake, 1 << 30, None) == -1
-    assert f(fake, fake, fake, fake, 32, 0, fake, None, cd, fake, 1 << 30, None) == -1
-    assert f(fake, fake, fake, fake, 32, 101, fake, None, cd, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 0, 10, fake, None, None, cd, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 129, 10, fake, None, None, cd, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 32, 0, fake, None, None, cd, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 32, 101, fake, None, None, cd, fake, 1 << 30, None) == -1
     # workspace too small
-    assert f(fake, fake, fake, fake, 32, 10, fake, None, cd, fake, 16, None) == -3
+    assert f(fake, fake, fake, fake, 32, 10, fake, None, None, cd, fake, 16, None) == -3
+    # scores_out misaligned
+    assert f(fake, fake, fake, fake, 32, 10, fake, None, odd, cd, fake, 1 << 30, None) == -1
+    assert "scores_out" in L.last_error()
     # desc null
-    assert f(fake, fake, fake, fake, 32, 10, fake, None, None, fake, 1 << 30, None) == -1
+    assert f(fake, fake, fake, fake, 32, 10, fake, None, None, None, fake, 1 << 30, None) == -1
 
 
 def test_other_entry_points_validate(L):
@@ -131,8 +134,8 @@ def test_other_entry_points_validate(L):
     assert lib.loki_attend(fake, fake, fake, fake, None, 10, fake, cd, fake, 8, None) == -3
     assert lib.loki_pack_kcache(fake, 129, fake, cd, None) == -1
     assert lib.loki_unpack_kcache(fake, -1, fake, cd, None) == -1
-    assert lib.loki_decode_append(fake, None, fake, fake, fake, fake, 32, 10, fake, None, cd,
-                                  fake, 1 << 30, None) == -1
+    assert lib.loki_decode_append(fake, None, fake, fake, fake, fake, 32, 10, fake, None, None,
+                                  cd, fake, 1 << 30, None) == -1
     fa = lib.loki_full_attention
     assert fa(fake, fake, fake, fake, None, cd, fake, 1 << 30, None) == -1  # out NULL
     assert fa(odd, fake, fake, fake, fake, cd, fake, 1 << 30, None) == -1   # misaligned q
@@ -172,4 +175,4 @@ def test_binding_has_no_cpu_path(L):
     d = _desc(L)
     q = torch.zeros((2, 4, 128), dtype=torch.float16)
     with pytest.raises(ValueError, match="device memory"):
-        L.decode(q, q, q, q, 32, 10, d, workspace=torch.zeros(1), out=torch.zeros(1))
+        L.decode(q, q, q, q, 32, 10, d, workspace=torch.zeros(1), out=torch.zeros((2, 4, 128)))

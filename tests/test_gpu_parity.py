@@ -742,3 +742,88 @@ def test_workload_full_size(L, name):
     if outs is not None:
         res = H.full_parity(wl, x, outs, idxs)
         H.log(f"  {name} (separate launches): {res}")
+
+
+# ----------------------------------------------------- output dtype, score output
+
+OUT16_CASES = {
+    "one-launch-g1-helpers": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1500, k=300),
+    "one-launch-g4": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, k=200),
+    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100),
+    "separate-f32": dict(dtype="f32", B=2, Hq=4, Hkv=4, S=5000, k=300),
+    "append-one-launch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1200, S_cap=1300, k=200,
+                              append=True),
+}
+TORCH16 = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", list(OUT16_CASES), ids=list(OUT16_CASES))
+def test_out_dtype(L, case, odt):
+    """A 16-bit output is the fp32 output of the same step rounded once to
+    nearest-even (torch's conversion), bit for bit."""
+    wl = _small(**OUT16_CASES[case])
+    H.log(f"out_dtype {odt} {case}: {W.describe(wl)}")
+    x = W.generate(wl)
+    outs = {}
+    for name, dt in (("f32", L.F32), (odt, L.NAME_CODE[odt])):
+        dev = H.upload(wl, x)   # fresh caches: the appending step rewrites row S-1
+        desc = dev["desc"].with_out_dtype(dt)
+        if wl.append:
+            outs[name] = L.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"],
+                                         dev["v"], dev["P"], wl.d, wl.k, desc)
+        else:
+            outs[name] = L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc)
+    torch.cuda.synchronize()
+    assert outs[odt].dtype == TORCH16[odt]
+    assert torch.equal(_bits(outs[odt]), _bits(outs["f32"].to(TORCH16[odt])))
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16"])
+@pytest.mark.parametrize("which", ["full", "pca"])
+def test_out_dtype_all_tokens(L, which, odt):
+    wl = _small("bf16", B=2, Hq=8, Hkv=4, S=1700, k=100)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    fn = (lambda desc: L.full_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], desc)) \
+        if which == "full" else \
+        (lambda desc: L.pca_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, desc))
+    o32 = fn(dev["desc"])
+    o16 = fn(dev["desc"].with_out_dtype(L.NAME_CODE[odt]))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o16), _bits(o32.to(TORCH16[odt])))
+
+
+@pytest.mark.parametrize("append", [False, True], ids=["decode", "decode_append"])
+def test_decode_scores_out(L, append):
+    """scores_out holds the low-dimensional scores the selection ranked: equal
+    to loki_score's on the same caches, and the returned sets are exactly
+    their top k (ties to the lower index)."""
+    wl = _small("f16", B=2, Hq=8, Hkv=4, S=1500, S_cap=1600, k=150, append=append)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    desc = dev["desc"]
+    assert L.decode_plan(desc, wl.d, wl.k, append)   # one launch without scores_out
+    sc = torch.full((wl.B, wl.Hq, wl.S), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.B, wl.Hq, wl.k), -7, dtype=torch.int32, device="cuda")
+    if append:
+        out = L.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"], dev["v"],
+                              dev["P"], wl.d, wl.k, desc, idx_out=idx, scores_out=sc)
+    else:
+        out = L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc,
+                       idx_out=idx, scores_out=sc)
+    qr = L.rotate_query(dev["q"], dev["P"], desc)
+    s2 = L.score(qr, dev["kcache"], wl.d, desc)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, s2)
+    s = sc.cpu().numpy().astype(np.float64)
+    g = idx.cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            assert np.array_equal(g[b, h], oracle.topk_rows(s[b, h][None], wl.k)[0])
+    res = H.full_parity(wl, x, out.cpu().numpy().astype(np.float64), g)
+    H.log(f"  scores_out {res}")
