@@ -9,7 +9,10 @@
 // it with 16-byte loads, LPT lanes per token (LPT = dp*elem/16), every lane
 // holding the matching fp32 slice of qr for each query head of the KV group;
 // the LPT partial dot products are summed with DPP.  One pass over the panel
-// serves all g query heads of a GQA group.
+// serves all g query heads of a GQA group.  With four lanes per token and
+// g <= 4, a tile's scores are staged in LDS and written at the end of the
+// tile in 16-byte stores: writes interleaved with the panel stream cost the
+// read stream more than one burst of whole lines.
 #include "loki_internal.h"
 
 namespace loki {
@@ -18,10 +21,17 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreBatch = 8;  // 16-byte loads per lane per batch; two batches in flight
+constexpr int kStageScores = 4096;  // scores of one tile staged in LDS (all g heads)
+
+// Tiles whose scores go through LDS: four lanes per token, g in {1, 2, 4}.
+template <int LPT, int G>
+constexpr bool kStaged = LPT == 4 && (G == 1 || G == 2 || G == 4);
 
 // One workgroup streams a tile of p.tile_tokens tokens of one (b, kv) panel.
 template <int DT, int LPT, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams p) {
+  constexpr bool STAGE = kStaged<LPT, G>;
+  __shared__ __align__(16) float stage[STAGE ? kStageScores : 1];  // [G][tile_tokens]
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int TPP = kScoreThreads / LPT;  // tokens per pass
   constexpr int NB = kScoreBatch;
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
         const float u1 = (b0 ? a[g0 + 3] : a[g0 + 2]) + dpp_f<0xB1>(b0 ? a[g0 + 2] : a[g0 + 3]);
         const float r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
         const int t = t0 + (pass0 + g0 + c) * TPP + tl;
-        if (t < t_end) srow[t] = r;
+        if (t < t_end) stage[t - t0] = r;
       }
       return;
     }
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
           r = u + dpp_f<0x4E>(u);
         }
         const int t = t0 + (pass0 + it) * TPP + tl;
-        if (t < t_end && c < G) srow[(size_t)c * sh.S + t] = r;
+        if (t < t_end && c < G) stage[c * p.tile_tokens + (t - t0)] = r;
       }
       return;
     }
@@ -147,6 +157,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
     consume(xb, pass + NB);
     if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
+  }
+  if constexpr (STAGE) {
+    // the tile's scores, head by head: 16-byte stores where the row allows
+    // (t0 is a multiple of the pass step, so it is 16-byte aligned when S is
+    // a multiple of 4), scalar stores for the rest
+    __syncthreads();
+    const int n = t_end - t0;
+    const int n4 = (sh.S % 4 == 0) ? n / 4 * 4 : 0;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float* dst = srow + (size_t)h * sh.S + t0;
+      const float* src = stage + h * p.tile_tokens;
+      for (int e = threadIdx.x * 4; e < n4; e += kScoreThreads * 4)
+        *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
+      for (int e = n4 + threadIdx.x; e < n; e += kScoreThreads) dst[e] = src[e];
+    }
   }
 }
 
@@ -177,7 +203,10 @@ hipError_t launch_lpt(ScoreParams p, hipStream_t st) {
   constexpr int STEP = (kScoreThreads / LPT) * 2 * kScoreBatch;
   const long long units = (long long)p.sh.B * p.sh.Hkv;
   long long want = (long long)p.sh.S * units / (p.sh.g > 1 ? 2048 : 512);
-  want = want < STEP ? STEP : (want > 4096 ? 4096 : want);
+  // staged tiles hold all g heads' scores of the tile in LDS
+  const bool staged = LPT == 4 && (p.sh.g == 1 || p.sh.g == 2 || p.sh.g == 4);
+  const long long cap = staged ? kStageScores / p.sh.g : 4096;
+  want = want < STEP ? STEP : (want > cap ? cap : want);
   p.tile_tokens = (int)((want + STEP - 1) / STEP * STEP);
   p.n_tiles = (p.sh.S + p.tile_tokens - 1) / p.tile_tokens;
   const dim3 grid((unsigned)((size_t)p.n_tiles * p.sh.B * p.sh.Hkv));
