@@ -827,3 +827,64 @@ def test_decode_scores_out(L, append):
             assert np.array_equal(g[b, h], oracle.topk_rows(s[b, h][None], wl.k)[0])
     res = H.full_parity(wl, x, out.cpu().numpy().astype(np.float64), g)
     H.log(f"  scores_out {res}")
+
+
+# ------------------------------------------------------------ graph capture
+
+GRAPH_CASES = {
+    "one-launch-g1": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1500, k=300),
+    "one-launch-g4": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, k=200),
+    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100),
+    "append-one-launch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1200, S_cap=1300, k=200,
+                              append=True),
+}
+
+
+@pytest.mark.parametrize("case", list(GRAPH_CASES), ids=list(GRAPH_CASES))
+def test_decode_graph_replay(L, case):
+    """The step captured into a HIP graph (torch.cuda.CUDAGraph) and replayed
+    several times, with eager work and synchronisations between the replays:
+    every replay equals the eager step bit for bit.  Under capture the
+    one-launch kernel runs without helper workgroups, so the eager reference
+    is taken with LOKI_FLAG_NO_HELPERS (the same kernel configuration)."""
+    wl = _small(**GRAPH_CASES[case])
+    H.log(f"graph replay {case}: {W.describe(wl)}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    desc = dev["desc"].with_flags(L.FLAG_NO_HELPERS)
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device="cuda")
+    ws = L.empty_workspace(desc, wl.d, wl.k)
+
+    def step(stream=None):
+        if wl.append:
+            L.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"], dev["v"],
+                            dev["P"], wl.d, wl.k, desc, out=out, idx_out=idx, workspace=ws,
+                            stream=stream)
+        else:
+            L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc, out=out,
+                     idx_out=idx, workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    out_e, idx_e = out.clone(), idx.clone()
+    res = H.full_parity(wl, x, out_e.cpu().numpy().astype(np.float64), idx_e.cpu().numpy())
+    H.log(f"  eager {res}")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)                      # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()                          # the capture stream is the current stream here
+    for rep in range(4):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_e), f"replay {rep}: outputs differ"
+        assert torch.equal(idx, idx_e), f"replay {rep}: index sets differ"
