@@ -83,8 +83,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the multi-GPU sharding is a design note, not built.",
+        print(f"bench.py: the Loki step here runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); sharding over several GPUs is described, not built.",
               file=sys.stderr, flush=True)
         sys.exit(2)
 

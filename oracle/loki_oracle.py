@@ -56,7 +56,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            from oracle import build as _b  # noqa: WPS433  (build the checker on first use)
+            from oracle import build as _b  # noqa: WPS433  (build the oracle library on first use)
             _b.build()
         L = ctypes.CDLL(LIB_PATH)
         vp, ip, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
