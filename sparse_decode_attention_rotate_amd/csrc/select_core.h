@@ -18,8 +18,10 @@
 //  2. The last taken element.  Elements are ordered by (order-preserving key
 //     descending, index ascending); the k-th one, (T, I), is found inside b*:
 //     with few members (the common case) one pass over the row collects them
-//     and counts, per wave, the members of higher bins, then one wave ranks
-//     the candidates with lane reads; otherwise radix passes over 8-bit digits
+//     and counts, per wave, the members of higher bins, then a candidate's
+//     rank is one ballot over all candidates (the waves take the candidates
+//     in turn; the fused kernel's select_rows ranks its few in one wave);
+//     otherwise radix passes over 8-bit digits
 //     of the members' keys (per-wave LDS histograms), then the position of the
 //     last taken key among equal keys, then a counting pass.
 //  3. Ordered compaction: element i is taken iff key > T or (key == T and
@@ -328,23 +330,25 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     if (lane == 0) sm.wcnt[wave] = (int)gt;
     __syncthreads();
-    if (wave == 0) {
-      // candidate m on lane m; rank = members ordered before it by
-      // (key descending, index ascending)
+    // rank of candidate c = members ordered before it by (key descending,
+    // index ascending): one ballot over the candidates on the lanes; the
+    // waves take the candidates in turn
+    {
       const bool mine = lane < nb;
       const unsigned mk = mine ? sm.cand_key[lane] : 0u;
       const int mi = mine ? sm.cand_idx[lane] : INT_MAX;
-      int rank = 0;
-      for (int m = 0; m < nb; m++) {
-        const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, m);
-        const int oi = __builtin_amdgcn_readlane(mi, m);
-        rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+      for (int c = wave; c < nb; c += NW) {
+        const unsigned ck = (unsigned)__builtin_amdgcn_readlane((int)mk, c);
+        const int ci = __builtin_amdgcn_readlane(mi, c);
+        const int rank = __popcll(__ballot(mine && (mk > ck || (mk == ck && mi < ci))));
+        if (lane == 0) {
+          if (rank == rem - 1) {  // exactly one candidate
+            sm.thr_key = ck;
+            sm.thr_idx = ci;
+          }
+          if (rank < rem) atomicAdd(&sm.wcnt[ci / row.per_wave], 1);
+        }
       }
-      if (mine && rank == rem - 1) {  // exactly one lane
-        sm.thr_key = mk;
-        sm.thr_idx = mi;
-      }
-      if (mine && rank < rem) atomicAdd(&sm.wcnt[mi / row.per_wave], 1);
     }
     __syncthreads();
   } else {
