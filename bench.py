@@ -65,9 +65,10 @@ def src_sha(name):
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic_<workload>.txt, lines "traffic {json}"), if
-    the counters were taken on the current source of that kernel; else None."""
+    """The counter record of `kernel` (HBM bytes per launch, read and written)
+    from the committed rocprofv3 summary (profiles/hbm_traffic_<workload>.txt,
+    lines "traffic {json}"), if the counters were taken on the current source
+    of that kernel; else None."""
     p = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
     if not os.path.exists(p):
         return None
@@ -75,7 +76,7 @@ def measured_traffic(workload, kernel):
         if line.startswith("traffic "):
             t = json.loads(line[len("traffic "):])
             if t.get("kernel") == kernel and t.get("src_sha") == src_sha(KERNEL_SOURCES[kernel]):
-                return t.get("hbm_bytes_per_launch")
+                return t
     return None
 
 
@@ -127,7 +128,7 @@ def main():
     one_launch = loki.decode_plan(desc, wl.d, wl.k, wl.append)
     vp = ctypes.c_void_p
 
-    def make_calls(d_):
+    def make_calls(d_, st_=stream):
         cd = d_.c()
         calls = []
         for kc, vc in sets:
@@ -136,7 +137,7 @@ def main():
                               (vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
                                vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d,
                                wl.k, vp(out.data_ptr()), None, None, ctypes.byref(cd),
-                               vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))))
+                               vp(ws.data_ptr()), ws.numel(), vp(st_.cuda_stream))))
             else:
                 # the step of the method: loki_decode(q, Kcache_rot, V, P, d, k, out);
                 # the optional index and score outputs are not requested
@@ -144,7 +145,7 @@ def main():
                               (vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
                                vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()),
                                None, None, ctypes.byref(cd), vp(ws.data_ptr()),
-                               ws.numel(), vp(stream.cuda_stream))))
+                               ws.numel(), vp(st_.cuda_stream))))
         return cd, calls
 
     # pre-marshalled C-ABI arguments, one tuple per cache copy
@@ -182,6 +183,60 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # spread: five more regions of K steps timed the same way (the value
+    # above is the first region's)
+    spread_us = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        spread_us.append(ev0.elapsed_time(ev1) / args.steps * 1e3)
+    spread_us.sort()
+    spread = {"regions": len(spread_us), "median_us": round(spread_us[len(spread_us) // 2], 2),
+              "p10_us": round(spread_us[0], 2), "p90_us": round(spread_us[-1], 2)}
+
+    # the step replayed from a HIP graph: one captured step per cache copy
+    graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            _, calls_cap = make_calls(desc, torch.cuda.current_stream())
+            for i in range(len(calls_cap)):
+                step(i, calls_cap)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(sets))
+        ev0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round(ev0.elapsed_time(ev1) / (reps * len(sets)) * 1e3, 2),
+                 "steps": reps * len(sets)}
+        del g
+    except Exception as e:  # reported, not fatal: the eager timing stands
+        graph = {"error": str(e)[:200]}
+
+    # the step once more on the first cache copy, with its index sets, for the
+    # oracle's check of sampled units (before any later measurement rewrites
+    # a cache row)
+    gpu = None
+    if not args.no_cpu_baseline:
+        idx_c = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device=dev)
+        fn, a = calls[0]
+        a = list(a)
+        a[9 if wl.append else 7] = vp(idx_c.data_ptr())
+        if fn(*a) != 0:
+            raise RuntimeError(f"decode failed: {loki.last_error()}")
+        torch.cuda.synchronize()
+        gpu = {"out": out.cpu().numpy().astype("float64"), "idx": idx_c.cpu().numpy()}
 
     # ---- separate launches: whole step, then each kernel alone, K back-to-back
     # launches between two events on the launch stream (as a kernel trace sees them)
@@ -354,7 +409,8 @@ def main():
         dom_us, dom_bytes = per_kernel[dom], per_kernel_bytes[dom]
         kernels = per_kernel
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name, dom)
+    trec = measured_traffic(wl.name, dom)
+    traffic = trec.get("hbm_bytes_per_launch") if trec else None
 
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -375,6 +431,8 @@ def main():
         "config": {**W.describe(wl), "algorithmic_bytes_per_step": alg_bytes,
                    "cache_copies_cycled": args.sets},
         "launch_plan": "one kernel" if one_launch else "separate kernels",
+        "spread": spread,
+        "graph": graph,
         "kernel_us": kernels,
         "separate_launches": {"us_per_step": round(sep_step_us, 2), "kernel_us": per_kernel},
         "full_attention": {"us_per_step": round(full_us, 2), "kv_bytes_per_step": full_bytes,
@@ -388,12 +446,16 @@ def main():
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "traffic_read": (round(trec["fetch_kib_per_launch"] * 1024 * trec["fetch_scale"])
+                                      if trec else None),
+                     "traffic_write": (round(trec["write_kib_per_launch"] * 1024 * trec["write_scale"])
+                                       if trec else None),
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(dom_us, 2)},
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, gpu)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20)
@@ -407,18 +469,50 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, x, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def set_omp_threads(n):
+    """Thread count of the OpenMP runtime the C oracle runs on (libgomp)."""
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        return True
+    except OSError:
+        return False
+
+
+# normwise output tolerance per storage dtype (fp32 vs 16-bit inputs)
+OUT_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def cpu_baseline(wl, x, budget_s, gpu=None):
     """The fp64 CPU oracle on the host cores, on a bounded sample of the same
-    step: whole (batch, head) units, as many as fit the time budget."""
+    step: whole (batch, head) units, as many as fit the time budget.  With
+    `gpu` (the step's output and index sets) the sampled units are also checked
+    against the oracle: index sets within the tie band of the oracle's
+    scores, outputs against the oracle's attention over the GPU's sets."""
     import numpy as np
     from oracle import loki_oracle as oracle
 
     n_units = wl.B * wl.Hq
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    krot, v = x["krot"][:, :, :wl.S], x["v"][:, :, :wl.S]
+    if wl.append:  # the cache after the step's own append (the oracle's rotation)
+        kr, vr = oracle.append_rows(x["k_new"], x["v_new"], x["P"], wl.dtype)
+        krot, v = krot.copy(), v.copy()
+        krot[:, :, wl.S - 1] = kr
+        v[:, :, wl.S - 1] = vr
     # calibrate on a few units, then size the sample to the budget
     probe = list(range(min(n_units, max(threads, 8))))
     t = time.time()
-    oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.k, wl.dtype, heads=probe)
+    oracle.decode(x["q"], krot, v, x["P"], wl.d, wl.k, wl.dtype, heads=probe)
     per_unit = (time.time() - t) / len(probe)
     n = int(min(n_units, max(len(probe), budget_s / max(per_unit, 1e-9) / 3)))
     heads = list(range(n))
@@ -428,19 +522,57 @@ def cpu_baseline(wl, x, budget_s):
     for _ in range(3):
         t = time.time()
         for _ in range(reps):
-            oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.k, wl.dtype, heads=heads)
+            r = oracle.decode(x["q"], krot, v, x["P"], wl.d, wl.k, wl.dtype, heads=heads)
         times.append((time.time() - t) / reps)
     sec = float(np.median(times))
     es = 4 if wl.dtype == "f32" else 2
     g = wl.Hq // wl.Hkv
-    # algorithmic bytes of the sampled units: S*d per query head's KV head share plus 2*k*D
-    sample_bytes = es * n * (wl.S * wl.d / g + 2 * wl.k * wl.D)
-    return {"value": round(sample_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} of {n_units} (batch, head) units of one step, fp64 C oracle, "
-                      f"median of 3 runs of {reps} repetitions ({sec:.3f} s per repetition), "
-                      f"OpenMP over units",
-            "seconds": round(sec, 3)}
+    # algorithmic bytes of a unit: S*d per query head's KV head share plus 2*k*D
+    unit_bytes = es * (wl.S * wl.d / g + 2 * wl.k * wl.D)
+    res = {"value": round(unit_bytes * n / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{n} of {n_units} (batch, head) units of one step, fp64 C oracle, "
+                     f"median of 3 runs of {reps} repetitions ({sec:.3f} s per repetition), "
+                     f"OpenMP over units",
+           "seconds": round(sec, 3)}
+    # one thread, on the first units of the sample (a few seconds)
+    if set_omp_threads(1):
+        n1 = max(1, min(n, int(max(1.0, budget_s / 10) / max(per_unit * threads, 1e-9))))
+        t = time.time()
+        oracle.decode(x["q"], krot, v, x["P"], wl.d, wl.k, wl.dtype, heads=list(range(n1)))
+        s1 = time.time() - t
+        set_omp_threads(threads)
+        res["one_thread"] = {"value": round(unit_bytes * n1 / s1 / 1e9, 4), "unit": "GB/s",
+                             "units": n1, "seconds": round(s1, 3)}
+    if gpu is not None:
+        # the sampled units of the GPU's step against the oracle
+        B, Hq = wl.B, wl.Hq
+        swaps = band_ok = 0
+        for u in heads:
+            b, h = divmod(u, Hq)
+            gi = gpu["idx"][b, h]
+            sc = r["scores"][b, h]
+            ok = (len(np.unique(gi)) == wl.k and gi.min() >= 0 and gi.max() < wl.S and
+                  bool(np.all(np.diff(gi) > 0)))
+            if ok and wl.k < wl.S:
+                srt = np.sort(sc)[::-1]
+                tau = 1e-3 * max(abs(srt[wl.k - 1]), 1e-3 * np.abs(sc).max())
+                mask = np.zeros(wl.S, bool)
+                mask[gi] = True
+                ok = sc[mask].min() >= sc[~mask].max() - tau
+                swaps += wl.k - len(np.intersect1d(gi, r["idx"][b, h]))
+            band_ok += int(ok)
+        ref = oracle.attend_given(x["q"], krot, v, x["P"], gpu["idx"], wl.dtype, heads=heads)
+        errs = []
+        for u in heads:
+            b, h = divmod(u, Hq)
+            errs.append(np.abs(gpu["out"][b, h] - ref[b, h]).max() /
+                        max(np.abs(ref[b, h]).max(), 1e-30))
+        res["parity"] = {"units": n, "index_sets_within_tie_band": band_ok,
+                         "swapped_tokens_within_band": int(swaps),
+                         "max_rel_out": float(f"{max(errs):.3e}"), "tolerance": OUT_TOL[wl.dtype],
+                         "ok": bool(band_ok == n and max(errs) < OUT_TOL[wl.dtype])}
+    return res
 
 
 if __name__ == "__main__":

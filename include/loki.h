@@ -104,8 +104,8 @@ typedef struct {
    run helpers: a helper repeats the selection of one of the units of the
    last round and attends the second half of its rows, and the two halves are
    merged (through the workspace).  Same index sets; outputs equal up to fp32
-   summation order.  Helpers are also off while `stream` is being captured
-   into a graph. */
+   summation order.  A captured launch replays correctly: the pair's flag is
+   cleared by the second of the two. */
 #define LOKI_FLAG_NO_HELPERS 2u
 
 /* Human-readable name of a status code; never NULL. */

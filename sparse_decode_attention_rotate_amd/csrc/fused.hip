@@ -475,9 +475,15 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     }
     wait_stores();
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0) {
       later = __hip_atomic_exchange(p.help_flag + pair, p.tag, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) == p.tag;
+      // both halves are in: the flag goes back to 0, so that the next launch
+      // on this workspace -- also a replay of a captured one, whose tag is the
+      // captured tag -- finds no tag there
+      if (later)
+        __hip_atomic_store(p.help_flag + pair, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (later && tid < D) {
       const float oM = ld_coherent(other), oL = ld_coherent(other + 1);

@@ -138,13 +138,6 @@ unsigned long long next_tag(const void* workspace) {
   return it->second;
 }
 
-// A graph replays its kernel arguments, tag included: no pairing under capture.
-bool stream_capturing(hipStream_t st) {
-  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &status) != hipSuccess) return true;
-  return status != hipStreamCaptureStatusNone;
-}
-
 // Compute units of the current device (cached per device).
 int compute_units() {
   static int cache[64] = {0};
@@ -228,7 +221,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     const int full = units / ncu, part = units % ncu;
     int n_help = 0;
     if (sh.g == 1 && k >= 256 && part > 0 && full + 1 <= per_cu &&
-        !(desc->flags & LOKI_FLAG_NO_HELPERS) && !stream_capturing(st))
+        !(desc->flags & LOKI_FLAG_NO_HELPERS))
       n_help = (part < ncu - part ? part : ncu - part) / 8 * 8;
     fp.n_help = n_help;
     fp.help_first = units - n_help;

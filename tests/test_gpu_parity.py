@@ -840,18 +840,19 @@ GRAPH_CASES = {
 }
 
 
+@pytest.mark.parametrize("helpers", [True, False], ids=["helpers", "no-helpers"])
 @pytest.mark.parametrize("case", list(GRAPH_CASES), ids=list(GRAPH_CASES))
-def test_decode_graph_replay(L, case):
+def test_decode_graph_replay(L, case, helpers):
     """The step captured into a HIP graph (torch.cuda.CUDAGraph) and replayed
     several times, with eager work and synchronisations between the replays:
-    every replay equals the eager step bit for bit.  Under capture the
-    one-launch kernel runs without helper workgroups, so the eager reference
-    is taken with LOKI_FLAG_NO_HELPERS (the same kernel configuration)."""
+    every replay equals the eager step bit for bit.  A replay reuses the
+    captured launch tag of the helper pairs; the second workgroup of a pair
+    clears the pair's flag, so every replay pairs afresh."""
     wl = _small(**GRAPH_CASES[case])
-    H.log(f"graph replay {case}: {W.describe(wl)}")
+    H.log(f"graph replay {case} helpers={helpers}: {W.describe(wl)}")
     x = W.generate(wl)
     dev = H.upload(wl, x)
-    desc = dev["desc"].with_flags(L.FLAG_NO_HELPERS)
+    desc = dev["desc"] if helpers else dev["desc"].with_flags(L.FLAG_NO_HELPERS)
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device="cuda")
     ws = L.empty_workspace(desc, wl.d, wl.k)
@@ -888,3 +889,8 @@ def test_decode_graph_replay(L, case):
         torch.cuda.synchronize()
         assert torch.equal(out, out_e), f"replay {rep}: outputs differ"
         assert torch.equal(idx, idx_e), f"replay {rep}: index sets differ"
+        # an eager step on the same workspace between replays (a fresh tag)
+        out.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_e), f"eager step after replay {rep}: outputs differ"
