@@ -71,6 +71,7 @@ struct SelectSmem {
   unsigned hist[kBins];
   unsigned whist[NW][256];
   float wmin[NW], wmax[NW];
+  float wsum[NW], wsq[NW];
   unsigned wtot[NW];
   int sel_bin, sel_gt, sel_eq, n_cand;
   unsigned cand_key[kFewCandidates];
@@ -516,6 +517,14 @@ __device__ __forceinline__ void write_rows_in_index_order(const int32_t* rows, i
   }
 }
 
+// Rows of more than 16384 scores (32 order keys per thread, or re-read
+// scores): a bin of the linear binning holds 8 or more scores on average, and
+// a few large outliers that stretch [min, max] crowd the bin of the k-th
+// score; these rows bin over mean +- 6 sd instead.  Shorter rows keep
+// [min, max] (the moments cost more there than the rare refinement).
+template <int KREG>
+constexpr bool kClampRange = KREG == 0 || KREG >= 32;
+
 // Whole selection from the scores alone (range, histogram, steps 1-3).
 // With have_range the caller passes the row's minimum and maximum.
 template <int NT, int KREG, typename Load>
@@ -529,31 +538,62 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
   select_clear<NT>(sm);
   float lo = lo_in, hi = hi_in;
   if (!have_range) {
-    // the range through the keys: integer min / max, padding excluded
+    // the range through the keys (integer min / max) and, for long rows,
+    // the first two moments of the scores; padding excluded
     unsigned kmin = 0xffffffffu, kmax = 0u;
+    float sum = 0.f, sq = 0.f;
     row.each([&](int i, unsigned key) {
       const bool valid = i < S;
       kmin = min(kmin, valid ? key : 0xffffffffu);
       kmax = max(kmax, valid ? key : 0u);
+      if constexpr (kClampRange<KREG>) {
+        // the empty asm keeps the compiler from holding these scores in
+        // registers for the histogram pass, which recomputes them
+        unsigned kk = key;
+        asm volatile("" : "+v"(kk));
+        const float v = valid ? key_score(kk) : 0.f;
+        sum += v;
+        sq = fmaf(v, v, sq);
+      }
     });
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       kmin = min(kmin, (unsigned)__shfl_xor((int)kmin, o, 64));
       kmax = max(kmax, (unsigned)__shfl_xor((int)kmax, o, 64));
     }
+    if constexpr (kClampRange<KREG>) {
+      sum = wave_sum(sum);
+      sq = wave_sum(sq);
+    }
     if (lane == 0) {
       sm.wmin[wave] = key_score(kmin);
       sm.wmax[wave] = key_score(kmax);
+      sm.wsum[wave] = sum;
+      sm.wsq[wave] = sq;
     }
   }
   __syncthreads();
   if (!have_range) {
     lo = sm.wmin[0];
     hi = sm.wmax[0];
+    float sum = sm.wsum[0], sq = sm.wsq[0];
 #pragma unroll
     for (int w = 1; w < NW; w++) {
       lo = fminf(lo, sm.wmin[w]);
       hi = fmaxf(hi, sm.wmax[w]);
+      sum += sm.wsum[w];
+      sq += sm.wsq[w];
+    }
+    if constexpr (kClampRange<KREG>) {
+      // bin over [mean - 6 sd, mean + 6 sd] within [min, max]: a few large
+      // outliers then no longer squeeze the bulk into few bins (scores
+      // outside land in the end bins, and clamped linear bins stay
+      // monotone).  A non-finite mean or spread leaves the range as it is
+      // (fmaxf / fminf return the non-NaN operand).
+      const float mean = sum / (float)S;
+      const float sd = sqrtf(fmaxf(sq / (float)S - mean * mean, 0.f));
+      lo = fmaxf(lo, mean - 6.f * sd);
+      hi = fminf(hi, mean + 6.f * sd);
     }
   }
   const float scale = bin_scale(lo, hi);
