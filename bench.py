@@ -43,7 +43,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_13b_f16")
-    ap.add_argument("--sets", type=int, default=3, help="independent cache copies cycled")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="independent cache copies cycled (default: max(3, 1 + "
+                         "ceil(512 MB / bytes one step reads)), so that every copy has "
+                         "left the 256 MB Infinity Cache before it is read again; 3 for "
+                         "steps that read less than 32 MB)")
     ap.add_argument("--settle", type=float, default=0.2,
                     help="seconds of untimed steps before the warm-up (steady clocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,6 +120,10 @@ def main():
     kc0 = loki.empty_kcache(desc)
     loki.pack_kcache(up(x["krot"]), kc0, desc.with_seq_len(wl.capacity))
     v0 = up(x["v"])
+    if args.sets <= 0:
+        # steps that read little are launch-bound: three copies are enough
+        step_bytes = wl.algorithmic_bytes()
+        args.sets = max(3, 1 + -(-(512 << 20) // step_bytes)) if step_bytes >= (32 << 20) else 3
     sets = [(kc0, v0)] + [(kc0.clone(), v0.clone()) for _ in range(args.sets - 1)]
     q = up(x["q"])
     P = torch.from_numpy(np.ascontiguousarray(x["P"])).to(dev)
