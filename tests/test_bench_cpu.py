@@ -1,0 +1,55 @@
+"""bench.py on the CPU: the one-GPU contract and the parity check of its
+cpu_baseline leg (fed with the oracle's own results, then with a corrupted
+output and a corrupted index set)."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+from oracle import loki_oracle as oracle  # noqa: E402
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_parity_check():
+    bench = _bench()
+    wl = W.custom(name="tiny", wid=400, B=1, Hq=4, Hkv=2, D=128, S=600, d=32, k=64,
+                  dtype="f16", tau=40.0, n_calib=2048)
+    x = W.generate(wl)
+    r = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.k, wl.dtype)
+    good = {"out": r["out"].copy(), "idx": r["idx"].copy()}
+    res = bench.cpu_baseline(wl, x, 0.3, good)
+    assert res["parity"]["ok"] and res["parity"]["units"] == 4
+    assert res["parity"]["max_rel_out"] == 0.0
+    # a wrong output
+    bad = {"out": good["out"].copy(), "idx": good["idx"]}
+    bad["out"][0, 1] *= 1.01
+    assert not bench.cpu_baseline(wl, x, 0.3, bad)["parity"]["ok"]
+    # a token far below the threshold in place of a selected one
+    bad = {"out": good["out"], "idx": good["idx"].copy()}
+    s = r["scores"][0, 2]
+    low = int(np.argmin(s))
+    row = bad["idx"][0, 2]
+    if low not in row:
+        row[np.argmin(s[row])] = low
+        row.sort()
+        res = bench.cpu_baseline(wl, x, 0.3, bad)["parity"]
+        assert res["index_sets_within_tie_band"] == 3 and not res["ok"]
