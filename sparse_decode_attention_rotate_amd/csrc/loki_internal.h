@@ -31,6 +31,9 @@ struct ProjectParams {
 
 struct ScoreParams {
   const float* qr;     // [B,Hq,D]
+  const void* q;       // [B,Hq,D] storage dtype, nullable: rotate q by P in the kernel
+  const float* P;      // [Hkv,D,D] (with q)
+  float* qr_out;       // [B,Hq,D] the rotated rows, written by each unit's first tile (with q)
   const void* kcache;
   float* scores;       // [B,Hq,S]
   int d;
@@ -113,6 +116,9 @@ struct LayoutParams {
 
 hipError_t launch_project(const ProjectParams& p, hipStream_t st);
 hipError_t launch_score(const ScoreParams& p, hipStream_t st);
+// Workgroups of the panel score kernel with four lanes per token (its staged
+// tiles) for this shape.
+long long score_workgroups_staged(const Shape& sh);
 hipError_t launch_topk(const TopkParams& p, int n_rows, hipStream_t st);
 hipError_t launch_attend(const AttendParams& p, hipStream_t st);
 hipError_t launch_layout(const LayoutParams& p, hipStream_t st);

@@ -9,7 +9,12 @@
 // it with 16-byte loads, LPT lanes per token (LPT = dp*elem/16), every lane
 // holding the matching fp32 slice of qr for each query head of the KV group;
 // the LPT partial dot products are summed with DPP.  One pass over the panel
-// serves all g query heads of a GQA group.  With four lanes per token and
+// serves all g query heads of a GQA group.  In a decode step the kernel can
+// also rotate the query itself (head_dim 128, staged tiles): each workgroup
+// forms the panel coordinates of its g rotated query rows from P's leading
+// columns while its first panel batches are in flight, and the first tile of
+// each (b, kv) also forms the remaining coordinates and writes the rotated
+// rows for the attention -- one launch fewer per step.  With four lanes per token and
 // g <= 4, a tile's scores are staged in LDS and written at the end of the
 // tile in 16-byte stores: writes interleaved with the panel stream cost the
 // read stream more than one burst of whole lines.
@@ -28,9 +33,10 @@ template <int LPT, int G>
 constexpr bool kStaged = LPT == 4 && (G == 1 || G == 2 || G == 4);
 
 // One workgroup streams a tile of p.tile_tokens tokens of one (b, kv) panel.
-template <int DT, int LPT, int G>
+template <int DT, int LPT, int G, bool ROT>
 __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams p) {
   constexpr bool STAGE = kStaged<LPT, G>;
+  static_assert(!ROT || STAGE, "the rotating variant is a staged one");
   __shared__ __align__(16) float stage[STAGE ? kStageScores : 1];  // [G][tile_tokens]
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int TPP = kScoreThreads / LPT;  // tokens per pass
@@ -62,15 +68,77 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   issue(xa, 0);
   issue(xb, NB);
 
-  // qr slices (issued after the first panel loads so both are in flight)
+  // the rotation (ROT): q rows staged as fp32, per-wave partial sums
+  constexpr int RD = 128;                              // head_dim of the rotating variant
+  constexpr int DP = LPT * 16 / Elem<DT>::kBytes;      // panel width
+  constexpr int NW = kScoreThreads / 64;
+  __shared__ float xq[ROT ? G : 1][RD];
+  __shared__ float qpart[ROT ? NW : 1][ROT ? G : 1][RD];
+  __shared__ float qs[ROT ? G : 1][DP];
+  const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query row of the group
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (ROT) {
+    // qs[h][0:DP] = q[h] . P[kv][:, 0:DP]: thread = (column quad, row slot)
+    constexpr int NQL = DP / 4, RSL = kScoreThreads / NQL, NL = RD / RSL;
+    const Rsrc Prs = make_rsrc(p.P + (size_t)kv * RD * RD, (uint32_t)(RD * RD * 4));
+    const int cql = tid % NQL, rsl = tid / NQL;
+    u32x4 pl[NL];
+#pragma unroll
+    for (int u = 0; u < NL; u++) pl[u] = load16(Prs, ((rsl + RSL * u) * RD + 4 * cql) * 4);
+    for (int e = tid; e < G * RD; e += kScoreThreads)
+      xq[e / RD][e % RD] = load_elem<DT>(p.q, q0 * RD + e);
+    __syncthreads();
+    float a[G][4];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NL; u++) {
+      float f[4];
+      unpack16<F32>(pl[u], f);
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        const float x = xq[h][rsl + RSL * u];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
+      }
+    }
+    // lanes of one column quad are NQL apart within the wave
+#pragma unroll
+    for (int o = NQL; o < 64; o <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], o, 64);
+    if (lane < NQL)
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) qpart[wave][h][4 * cql + cc] = a[h][cc];
+    __syncthreads();
+    for (int e = tid; e < G * DP; e += kScoreThreads) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; w++) s += qpart[w][e / DP][e % DP];
+      qs[e / DP][e % DP] = s;
+    }
+    __syncthreads();
+  }
+
+  // qr slices (read after the first panel loads are issued, so that both are
+  // in flight)
   float qv[G][E];
 #pragma unroll
   for (int h = 0; h < G; h++) {
-    const float* qrow = p.qr + ((size_t)b * sh.Hq + (size_t)kv * G + h) * sh.D;
 #pragma unroll
     for (int e = 0; e < E; e++) {
       const int j = c * E + e;  // < dp <= D: always inside the row
-      const float v = qrow[j];
+      float v;
+      if constexpr (ROT)
+        v = qs[h][j];
+      else
+        v = p.qr[(q0 + h) * sh.D + j];
       qv[h][e] = (j < p.d) ? v : 0.f;
     }
   }
@@ -158,6 +226,59 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     consume(xb, pass + NB);
     if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
   }
+  if constexpr (ROT) {
+    // the first tile of each (b, kv): the remaining coordinates,
+    // qs[h][DP:RD] = q[h] . P[kv][:, DP:RD] (32 quad slots x 8 row slots), and
+    // the rotated rows for the attention
+    if (tile == 0) {
+      constexpr int NQR = (RD - DP) / 4, RSR = kScoreThreads / 32, NR = RD / RSR;
+      static_assert(NQR <= 32, "quad slots");
+      const int cqr = tid % 32, rsr = tid / 32;
+      const Rsrc Prs = make_rsrc(p.P + (size_t)kv * RD * RD, (uint32_t)(RD * RD * 4));
+      u32x4 pr[NR];
+#pragma unroll
+      for (int u = 0; u < NR; u++)
+        pr[u] = load16(Prs, cqr < NQR ? ((rsr + RSR * u) * RD + DP + 4 * cqr) * 4 : kOutOfRange);
+      float a[G][4];
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] = 0.f;
+#pragma unroll
+      for (int u = 0; u < NR; u++) {
+        float f[4];
+        unpack16<F32>(pr[u], f);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+          const float x = xq[h][rsr + RSR * u];
+#pragma unroll
+          for (int cc = 0; cc < 4; cc++) a[h][cc] = fmaf(x, f[cc], a[h][cc]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) a[h][cc] += __shfl_xor(a[h][cc], 32, 64);
+      if (lane < 32 && cqr < NQR)
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+          for (int cc = 0; cc < 4; cc++) qpart[wave][h][DP + 4 * cqr + cc] = a[h][cc];
+      __syncthreads();
+      for (int e = tid; e < G * RD; e += kScoreThreads) {
+        const int h = e / RD, j = e % RD;
+        float s;
+        if (j < DP) {
+          s = qs[h][j];
+        } else {
+          s = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; w++) s += qpart[w][h][j];
+        }
+        p.qr_out[(q0 + h) * RD + j] = s;
+      }
+    }
+  }
   if constexpr (STAGE) {
     // the tile's scores, head by head: 16-byte stores where the row allows
     // (t0 is a multiple of the pass step, so it is 16-byte aligned when S is
@@ -195,26 +316,41 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
   }
 }
 
+// Tokens per tile of the panel kernel with LPT lanes per token: up to 4096
+// (256 KB of an fp16 panel), smaller when that leaves fewer than two
+// workgroups per compute unit (eight when a tile also writes the scores of
+// several heads); multiples of two batches; staged tiles hold all g heads'
+// scores of the tile in LDS.
+int tile_tokens(const Shape& sh, int lpt) {
+  const int step = (kScoreThreads / lpt) * 2 * kScoreBatch;
+  const long long units = (long long)sh.B * sh.Hkv;
+  long long want = (long long)sh.S * units / (sh.g > 1 ? 2048 : 512);
+  const bool staged = lpt == 4 && (sh.g == 1 || sh.g == 2 || sh.g == 4);
+  const long long cap = staged ? kStageScores / sh.g : 4096;
+  want = want < step ? step : (want > cap ? cap : want);
+  return (int)((want + step - 1) / step * step);
+}
+
 template <int DT, int LPT>
 hipError_t launch_lpt(ScoreParams p, hipStream_t st) {
-  // tiles of up to 4096 tokens (256 KB of an fp16 panel), smaller when that
-  // leaves fewer than two workgroups per compute unit (eight when a tile also
-  // writes the scores of several heads); multiples of two batches
-  constexpr int STEP = (kScoreThreads / LPT) * 2 * kScoreBatch;
-  const long long units = (long long)p.sh.B * p.sh.Hkv;
-  long long want = (long long)p.sh.S * units / (p.sh.g > 1 ? 2048 : 512);
-  // staged tiles hold all g heads' scores of the tile in LDS
-  const bool staged = LPT == 4 && (p.sh.g == 1 || p.sh.g == 2 || p.sh.g == 4);
-  const long long cap = staged ? kStageScores / p.sh.g : 4096;
-  want = want < STEP ? STEP : (want > cap ? cap : want);
-  p.tile_tokens = (int)((want + STEP - 1) / STEP * STEP);
+  p.tile_tokens = tile_tokens(p.sh, LPT);
   p.n_tiles = (p.sh.S + p.tile_tokens - 1) / p.tile_tokens;
   const dim3 grid((unsigned)((size_t)p.n_tiles * p.sh.B * p.sh.Hkv));
+  if constexpr (LPT == 4) {
+    if (p.q) {  // the rotating variant (head_dim 128, g in {1, 2, 4}: checked by the caller)
+      switch (p.sh.g) {
+        case 1: score_panel_kernel<DT, LPT, 1, true><<<grid, kScoreThreads, 0, st>>>(p); break;
+        case 2: score_panel_kernel<DT, LPT, 2, true><<<grid, kScoreThreads, 0, st>>>(p); break;
+        default: score_panel_kernel<DT, LPT, 4, true><<<grid, kScoreThreads, 0, st>>>(p); break;
+      }
+      return hipGetLastError();
+    }
+  }
   switch (p.sh.g) {
-    case 1: score_panel_kernel<DT, LPT, 1><<<grid, kScoreThreads, 0, st>>>(p); break;
-    case 2: score_panel_kernel<DT, LPT, 2><<<grid, kScoreThreads, 0, st>>>(p); break;
-    case 4: score_panel_kernel<DT, LPT, 4><<<grid, kScoreThreads, 0, st>>>(p); break;
-    default: score_panel_kernel<DT, LPT, 8><<<grid, kScoreThreads, 0, st>>>(p); break;
+    case 1: score_panel_kernel<DT, LPT, 1, false><<<grid, kScoreThreads, 0, st>>>(p); break;
+    case 2: score_panel_kernel<DT, LPT, 2, false><<<grid, kScoreThreads, 0, st>>>(p); break;
+    case 4: score_panel_kernel<DT, LPT, 4, false><<<grid, kScoreThreads, 0, st>>>(p); break;
+    default: score_panel_kernel<DT, LPT, 8, false><<<grid, kScoreThreads, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -240,6 +376,11 @@ hipError_t launch_dt(ScoreParams p, hipStream_t st) {
 }
 
 }  // namespace
+
+long long score_workgroups_staged(const Shape& sh) {
+  const long long n_tiles = (sh.S + tile_tokens(sh, 4) - 1) / tile_tokens(sh, 4);
+  return n_tiles * sh.B * sh.Hkv;
+}
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t st) {
   switch (p.sh.dtype) {

@@ -800,9 +800,10 @@ def test_out_dtype_all_tokens(L, which, odt):
 
 @pytest.mark.parametrize("append", [False, True], ids=["decode", "decode_append"])
 def test_decode_scores_out(L, append):
-    """scores_out holds the low-dimensional scores the selection ranked: equal
-    to loki_score's on the same caches, and the returned sets are exactly
-    their top k (ties to the lower index)."""
+    """scores_out holds the low-dimensional scores the selection ranked: the
+    returned sets are exactly their top k (ties to the lower index), and they
+    equal loki_score's on the same caches up to fp32 rounding (the step may
+    rotate the query inside its score kernel, with another summation order)."""
     wl = _small("f16", B=2, Hq=8, Hkv=4, S=1500, S_cap=1600, k=150, append=append)
     x = W.generate(wl)
     dev = H.upload(wl, x)
@@ -819,7 +820,9 @@ def test_decode_scores_out(L, append):
     qr = L.rotate_query(dev["q"], dev["P"], desc)
     s2 = L.score(qr, dev["kcache"], wl.d, desc)
     torch.cuda.synchronize()
-    assert torch.equal(sc, s2)
+    assert torch.isfinite(sc).all()
+    scale = s2.abs().amax(dim=-1, keepdim=True)
+    assert ((sc - s2).abs() <= 1e-5 * scale).all()
     s = sc.cpu().numpy().astype(np.float64)
     g = idx.cpu().numpy()
     for b in range(wl.B):
