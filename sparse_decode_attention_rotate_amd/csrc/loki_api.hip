@@ -234,16 +234,16 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     return hip_status(launch_fused(fp, st), "fused");
   }
 
-  // Without an append, and for the score kernel's staged tiles (head_dim 128,
-  // four lanes per token, 1, 2 or 4 query heads per KV head), the score
-  // kernel can rotate the query itself and write qr for the attention: no
-  // separate rotation launch.  Every score workgroup repeats the rotation of
-  // its heads' panel coordinates, which pays when the grid is one round of
-  // resident workgroups (four per compute unit), not when its tiles make
-  // several rounds (measured: 13B separate step 79.5 -> 71.4 us; GQA, 2048
+  // For the score kernel's staged tiles (head_dim 128, four lanes per token,
+  // 1, 2 or 4 query heads per KV head), the score kernel can rotate the query
+  // itself, write qr for the attention and do the append: no separate
+  // rotation launch.  Every score workgroup repeats the rotation of its heads'
+  // panel coordinates, which pays when the grid is one round of resident
+  // workgroups (four per compute unit), not when its tiles make several
+  // rounds (measured: 13B separate step 79.5 -> 71.4 us; GQA, 2048
   // workgroups, 140.4 -> 142.2 us).
   const int lpt = sh.dp * elem_bytes(sh.dtype) / 16;
-  const bool rotate_in_score = !append && sh.D == 128 && lpt == 4 && d <= sh.dp &&
+  const bool rotate_in_score = sh.D == 128 && lpt == 4 && d <= sh.dp &&
                                (sh.g == 1 || sh.g == 2 || sh.g == 4) &&
                                score_workgroups_staged(sh) <= 4LL * compute_units();
   if (!rotate_in_score) {
@@ -266,6 +266,12 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     sp.q = q;
     sp.P = P;
     sp.qr_out = qr;
+    if (append) {
+      sp.k_new = k_new;
+      sp.v_new = v_new;
+      sp.kcache_w = kcache;
+      sp.vcache_w = vcache;
+    }
   }
   sp.kcache = kcache;
   sp.scores = scores;

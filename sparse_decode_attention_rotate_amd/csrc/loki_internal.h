@@ -34,6 +34,10 @@ struct ScoreParams {
   const void* q;       // [B,Hq,D] storage dtype, nullable: rotate q by P in the kernel
   const float* P;      // [Hkv,D,D] (with q)
   float* qr_out;       // [B,Hq,D] the rotated rows, written by each unit's first tile (with q)
+  const void* k_new;   // [B,Hkv,D] nullable (with q): appended as token S-1 by each unit's last tile
+  const void* v_new;   // [B,Hkv,D]
+  void* kcache_w;      // the caches, written at row S-1 when appending
+  void* vcache_w;
   const void* kcache;
   float* scores;       // [B,Hq,S]
   int d;

@@ -14,7 +14,11 @@
 // forms the panel coordinates of its g rotated query rows from P's leading
 // columns while its first panel batches are in flight, and the first tile of
 // each (b, kv) also forms the remaining coordinates and writes the rotated
-// rows for the attention -- one launch fewer per step.  With four lanes per token and
+// rows for the attention -- one launch fewer per step.  With an append the
+// last tile of each (b, kv) rotates the new key as one more row, writes row
+// S-1 of both caches (the attention, a later launch, reads it there) and
+// replaces the new token's score by the one formed from the rounded row it
+// wrote, with the stream's per-lane partials and pairwise sums.  With four lanes per token and
 // g <= 4, a tile's scores are staged in LDS and written at the end of the
 // tile in 16-byte stores: writes interleaved with the panel stream cost the
 // read stream more than one burst of whole lines.
@@ -72,11 +76,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   constexpr int RD = 128;                              // head_dim of the rotating variant
   constexpr int DP = LPT * 16 / Elem<DT>::kBytes;      // panel width
   constexpr int NW = kScoreThreads / 64;
-  __shared__ float xq[ROT ? G : 1][RD];
-  __shared__ float qpart[ROT ? NW : 1][ROT ? G : 1][RD];
+  __shared__ float xq[ROT ? G + 1 : 1][RD];          // query rows, then the new key
+  __shared__ float qpart[ROT ? NW : 1][ROT ? G + 1 : 1][RD];
   __shared__ float qs[ROT ? G : 1][DP];
+  __shared__ float kn[ROT ? DP : 1];                  // new key's panel coordinates as stored
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query row of the group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool last = ROT && p.k_new != nullptr && t_end == sh.S;  // this tile appends token S-1
   if constexpr (ROT) {
     // qs[h][0:DP] = q[h] . P[kv][:, 0:DP]: thread = (column quad, row slot)
     constexpr int NQL = DP / 4, RSL = kScoreThreads / NQL, NL = RD / RSL;
@@ -87,6 +93,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     for (int u = 0; u < NL; u++) pl[u] = load16(Prs, ((rsl + RSL * u) * RD + 4 * cql) * 4);
     for (int e = tid; e < G * RD; e += kScoreThreads)
       xq[e / RD][e % RD] = load_elem<DT>(p.q, q0 * RD + e);
+    if (last)
+      for (int e = tid; e < RD; e += kScoreThreads) xq[G][e] = load_elem<DT>(p.k_new, head * RD + e);
     __syncthreads();
     float a[G][4];
 #pragma unroll
@@ -116,6 +124,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       for (int h = 0; h < G; h++)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) qpart[wave][h][4 * cql + cc] = a[h][cc];
+    if (last) {  // the new key's panel coordinates, from the same P loads
+      float ak[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NL; u++) {
+        float f[4];
+        unpack16<F32>(pl[u], f);
+        const float x = xq[G][rsl + RSL * u];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) ak[cc] = fmaf(x, f[cc], ak[cc]);
+      }
+#pragma unroll
+      for (int o = NQL; o < 64; o <<= 1)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) ak[cc] += __shfl_xor(ak[cc], o, 64);
+      if (lane < NQL)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) qpart[wave][G][4 * cql + cc] = ak[cc];
+    }
     __syncthreads();
     for (int e = tid; e < G * DP; e += kScoreThreads) {
       float s = 0.f;
@@ -123,6 +149,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       for (int w = 0; w < NW; w++) s += qpart[w][e / DP][e % DP];
       qs[e / DP][e % DP] = s;
     }
+    if (last)
+      for (int j = tid; j < DP; j += kScoreThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) s += qpart[w][G][j];
+        store_elem<DT>(p.kcache_w, head * sh.kl.head_elems + (size_t)(sh.S - 1) * DP + j, s);
+        kn[j] = stored_value<DT>(s);
+      }
     __syncthreads();
   }
 
@@ -227,6 +261,55 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
   }
   if constexpr (ROT) {
+    if (last) {
+      // the rest of the new key's row and its value row
+      constexpr int NQR = (RD - DP) / 4, RSR = kScoreThreads / 32, NR = RD / RSR;
+      const int cqr = tid % 32, rsr = tid / 32;
+      const Rsrc Prs = make_rsrc(p.P + (size_t)kv * RD * RD, (uint32_t)(RD * RD * 4));
+      u32x4 pr[NR];
+#pragma unroll
+      for (int u = 0; u < NR; u++)
+        pr[u] = load16(Prs, cqr < NQR ? ((rsr + RSR * u) * RD + DP + 4 * cqr) * 4 : kOutOfRange);
+      float ak[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NR; u++) {
+        float f[4];
+        unpack16<F32>(pr[u], f);
+        const float x = xq[G][rsr + RSR * u];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) ak[cc] = fmaf(x, f[cc], ak[cc]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) ak[cc] += __shfl_xor(ak[cc], 32, 64);
+      if (lane < 32 && cqr < NQR)
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) qpart[wave][G][DP + 4 * cqr + cc] = ak[cc];
+      __syncthreads();  // also: every stream store of this tile's scores is in LDS
+      for (int j = DP + tid; j < RD; j += kScoreThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) s += qpart[w][G][j];
+        store_elem<DT>(p.kcache_w, head * sh.kl.head_elems + sh.kl.rest_off +
+                                       (size_t)(sh.S - 1) * (RD - DP) + (j - DP), s);
+      }
+      for (int j = tid; j < RD; j += kScoreThreads)
+        copy_elem<DT>(p.vcache_w, (head * sh.S_cap + (size_t)(sh.S - 1)) * RD + j, p.v_new,
+                      head * RD + j);
+      // the new token's score from its stored panel coordinates: lane (h, cl)
+      // of wave 0 forms the partial over [cl*E, cl*E + E), group_sum adds the
+      // four partials pairwise (the stream's reduce-scatter adds the same pairs)
+      if (wave == 0) {
+        const int h = min(lane / LPT, G - 1), cl = lane % LPT;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) {
+          const int j = cl * E + e;
+          acc = fmaf(j < p.d ? qs[h][j] : 0.f, kn[j], acc);
+        }
+        acc = group_sum<LPT>(acc);
+        if (lane < G * LPT && cl == 0) stage[h * p.tile_tokens + (sh.S - 1 - t0)] = acc;
+      }
+    }
     // the first tile of each (b, kv): the remaining coordinates,
     // qs[h][DP:RD] = q[h] . P[kv][:, DP:RD] (32 quad slots x 8 row slots), and
     // the rotated rows for the attention
