@@ -362,11 +362,13 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   __syncthreads();
 
   // ---- 2. top-k of each head's scores, from LDS
-  // Single head (k within the per-wave list capacity): the selected rows come
-  // in two index-ordered parts and the attention starts as soon as they are
-  // known; the partial rotation sums go to LDS inside the selection's barriers.
+  // Single head (the per-wave lists hold every row above the threshold bin):
+  // the selected rows come in two index-ordered parts and the attention
+  // starts as soon as they are known; the partial rotation sums go to LDS
+  // inside the selection's barriers.
   constexpr bool kStreamRows = G == 1;
-  const bool stream_rows = kStreamRows && k <= kBins / NW;
+  const bool stream_rows =
+      kStreamRows && (KREG * 64 <= kRowListCap<NT> || k - 1 <= kRowListCap<NT>);
   auto rotate_rest = [&]() {  // qpart[w][h][DP:D] from the P loads in flight
     float a[GR][4];
 #pragma unroll

@@ -381,20 +381,30 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
   });
 }
 
+// Entries of each wave's list in select_rows: the lists fill sm.hist and
+// sm.whist, which lie back to back (the scan is done with the first, the
+// radix passes start on the second only after the lists are copied out).
+template <int NT>
+constexpr int kRowListCap = kBins / (NT / 64) + 256;
+
 // Selection for a caller that attends over the selected rows right away.
 // Rows [0, sel_gt) are the members of the bins above b*, in index order: one
-// pass appends them to per-wave lists kept in sm.hist (the scan no longer
-// needs it) while it collects b*'s members; rows [sel_gt, k) are the taken
-// members of b*, also in index order.  mid() runs between that pass and the
-// barrier after it.  Writes rows_idx / rows_val (score, -0 as +0) [0, k) and
-// sm.sel_gt; the caller needs a barrier before reading them.
-// Requires k <= kBins / (NT / 64) (the lists' capacity).
+// pass appends them to per-wave lists kept in sm.hist / sm.whist (the scan
+// no longer needs them) while it collects b*'s members; rows [sel_gt, k) are
+// the taken members of b*, also in index order.  mid() runs between that
+// pass and the barrier after it.  Writes rows_idx / rows_val (score, -0 as
+// +0) [0, k) and sm.sel_gt; the caller needs a barrier before reading them.
+// Requires that no wave's list outgrows kRowListCap<NT>: a list holds fewer
+// than k entries and at most a wave's share of the row (KREG * 64), so
+// k - 1 <= kRowListCap<NT> or KREG * 64 <= kRowListCap<NT> suffices.
 template <int NT, int KREG, typename Load, typename Mid>
 __device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k, int32_t* rows_idx,
                                             float* rows_val, SelectSmem<NT / 64>& sm, float lo,
                                             float scale, Mid&& mid) {
   constexpr int NW = NT / 64;
-  constexpr int CAP = kBins / NW;  // > sel_gt >= the length of any wave's list
+  constexpr int CAP = kRowListCap<NT>;  // >= the length of any wave's list
+  static_assert(sizeof(SelectSmem<NW>::hist) + sizeof(SelectSmem<NW>::whist) >=
+                    sizeof(int) * (size_t)NW * CAP, "lists fit hist and whist");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = row.S;
 
@@ -465,6 +475,7 @@ __device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k,
       }
     }
   } else {
+    __syncthreads();  // every list entry is copied out before whist is reused
     radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm);
     const unsigned T = sm.thr_key;
     const int I = sm.thr_idx;
