@@ -68,14 +68,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       x[it] = load16_stream(prs, t < t_end ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
     }
   };
-  u32x4 xa[NB], xb[NB];
-  issue(xa, 0);
-  issue(xb, NB);
-
   // the rotation (ROT): q rows staged as fp32, per-wave partial sums
   constexpr int RD = 128;                              // head_dim of the rotating variant
   constexpr int DP = LPT * 16 / Elem<DT>::kBytes;      // panel width
   constexpr int NW = kScoreThreads / 64;
+  constexpr int NQL = DP / 4, RSL = kScoreThreads / NQL, NL = RD / RSL;
+  constexpr int NXV = ROT ? ((G + 1) * RD + kScoreThreads - 1) / kScoreThreads : 1;
   __shared__ float xq[ROT ? G + 1 : 1][RD];          // query rows, then the new key
   __shared__ float qpart[ROT ? NW : 1][ROT ? G + 1 : 1][RD];
   __shared__ float qs[ROT ? G : 1][DP];
@@ -83,18 +81,34 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query row of the group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool last = ROT && p.k_new != nullptr && t_end == sh.S;  // this tile appends token S-1
+  // The rotation's loads go out before the panel batches: a wave's loads
+  // complete in issue order, so the rotation does not wait for the panel.
+  const int cql = tid % NQL, rsl = tid / NQL;
+  u32x4 pl[ROT ? NL : 1];
+  float xv[NXV];
   if constexpr (ROT) {
-    // qs[h][0:DP] = q[h] . P[kv][:, 0:DP]: thread = (column quad, row slot)
-    constexpr int NQL = DP / 4, RSL = kScoreThreads / NQL, NL = RD / RSL;
     const Rsrc Prs = make_rsrc(p.P + (size_t)kv * RD * RD, (uint32_t)(RD * RD * 4));
-    const int cql = tid % NQL, rsl = tid / NQL;
-    u32x4 pl[NL];
 #pragma unroll
     for (int u = 0; u < NL; u++) pl[u] = load16(Prs, ((rsl + RSL * u) * RD + 4 * cql) * 4);
-    for (int e = tid; e < G * RD; e += kScoreThreads)
-      xq[e / RD][e % RD] = load_elem<DT>(p.q, q0 * RD + e);
-    if (last)
-      for (int e = tid; e < RD; e += kScoreThreads) xq[G][e] = load_elem<DT>(p.k_new, head * RD + e);
+#pragma unroll
+    for (int u = 0; u < NXV; u++) {
+      const int e = tid + u * kScoreThreads;  // query rows, then the new key's row
+      // (both offsets are clamped into their rows: every lane's address is valid)
+      xv[u] = e < G * RD ? load_elem<DT>(p.q, q0 * RD + min(e, G * RD - 1))
+                         : (last ? load_elem<DT>(p.k_new, head * RD + min(max(e - G * RD, 0), RD - 1))
+                                 : 0.f);
+    }
+  }
+  u32x4 xa[NB], xb[NB];
+  issue(xa, 0);
+  issue(xb, NB);
+  if constexpr (ROT) {
+    // qs[h][0:DP] = q[h] . P[kv][:, 0:DP]: thread = (column quad, row slot)
+#pragma unroll
+    for (int u = 0; u < NXV; u++) {
+      const int e = tid + u * kScoreThreads;
+      if (e < (G + 1) * RD) xq[e / RD][e % RD] = xv[u];
+    }
     __syncthreads();
     float a[G][4];
 #pragma unroll
