@@ -77,20 +77,71 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
   }
 }
 
+// Merges the splits of one row: M = max of the splits' maxima, each split
+// weighted by 2^(m_s - M), added in split order.  The kernel is all latency
+// (a few hundred KB of partials, written by other XCDs, so not in this
+// XCD's L2): the first block's (m, l) and the first batch of accumulators
+// are loaded together, and each later batch of kBatch splits is one round
+// trip instead of one per split.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
+  constexpr int kBatch = 8;
+  constexpr int kWaves = D / 64;
+  __shared__ float sw[D], sl[D], smax[kWaves];
+  const int tid = threadIdx.x, ns = p.nsplit;
   const size_t bh = blockIdx.x;
-  const float* part = p.part + bh * p.nsplit * (size_t)(D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; s++) M = fmaxf(M, part[s * (D + 2)]);
-  float L = 0.f, a = 0.f;
-  for (int s = 0; s < p.nsplit; s++) {
-    const float* ps = part + s * (D + 2);
-    const float w = ps[0] == -INFINITY ? 0.f : exp2f(ps[0] - M);
-    L = fmaf(ps[1], w, L);
-    a = fmaf(ps[2 + threadIdx.x], w, a);
+  const size_t stride = D + 2;
+  const float* part = p.part + bh * ns * stride;
+
+  float mo = -INFINITY, lo = 0.f;
+  if (tid < ns) {
+    mo = part[tid * stride];
+    lo = part[tid * stride + 1];
   }
-  store_out(p.out, bh * D + threadIdx.x, a / L, p.sh.odt);
+  float v[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; j++) v[j] = j < ns ? part[j * stride + 2 + tid] : 0.f;
+  float m = mo;
+  for (int s = tid + D; s < ns; s += D) m = fmaxf(m, part[s * stride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) smax[tid >> 6] = m;
+  __syncthreads();
+  float M = smax[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; w++) M = fmaxf(M, smax[w]);
+
+  float L = 0.f, a = 0.f;
+  for (int b0 = 0; b0 < ns; b0 += D) {
+    if (b0 > 0) {
+      __syncthreads();  // every thread is done with the previous block's weights
+      mo = -INFINITY;
+      lo = 0.f;
+      if (b0 + tid < ns) {
+        mo = part[(b0 + tid) * stride];
+        lo = part[(b0 + tid) * stride + 1];
+      }
+    }
+    sw[tid] = mo == -INFINITY ? 0.f : exp2f(mo - M);
+    sl[tid] = lo;
+    __syncthreads();
+    const int nb = min(D, ns - b0);
+    for (int j0 = 0; j0 < nb; j0 += kBatch) {
+      if (b0 + j0 > 0) {  // the first batch was loaded up front
+#pragma unroll
+        for (int j = 0; j < kBatch; j++)
+          v[j] = j0 + j < nb ? part[(b0 + j0 + j) * stride + 2 + tid] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; j++) {
+        if (j0 + j < nb) {
+          L = fmaf(sl[j0 + j], sw[j0 + j], L);
+          a = fmaf(v[j], sw[j0 + j], a);
+        }
+      }
+    }
+  }
+  store_out(p.out, bh * D + tid, a / L, p.sh.odt);
 }
 
 template <int DT, int D>

@@ -627,6 +627,24 @@ def test_full_attention(L, dtype, Hq, Hkv, S):
     assert H.rel_err_rows(out, ref).max() < H.OUT_TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,S", [("bf16", 2, 2, 1, 5000), ("f16", 1, 2, 2, 70000)])
+def test_full_attention_many_splits(L, dtype, B, Hq, Hkv, S):
+    """Dense attention whose rows are split into more partials than one
+    batch of the merge (10 splits of 512 tokens) and than one block of it
+    (137 splits: more than head_dim, ragged last batch)."""
+    wl = _small(dtype, B=B, Hq=Hq, Hkv=Hkv, S=S, k=300, d=32)
+    H.log(f"full attention {dtype} B={B} Hq={Hq} Hkv={Hkv} S={S}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    out = L.full_attention(dev["q"], dev["kcache"], dev["v"], dev["P"], dev["desc"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    ref = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.D, S, dtype)["out"]
+    err = H.rel_err_rows(out, ref)
+    H.log(f"  max rel err {err.max():.3e}")
+    assert err.max() < H.OUT_TOL[dtype]
+
+
 # ----------------------------------------------------------------- PCAAttn
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,S,d,dp,D", [
