@@ -609,6 +609,36 @@ def test_helpers_with_dirty_workspace(L, fill):
     H.log(f"  dirty workspace ({fill}): {res}")
 
 
+@pytest.mark.parametrize("separate", [False, True], ids=["default", "separate"])
+def test_concurrent_streams_distinct_workspaces(L, separate):
+    """Two streams (default priority), each with its own workspace and
+    outputs, stepping at the same time over the same caches: the library keeps
+    no state between calls beyond each workspace's launch tags, so every step
+    equals the step run alone, bit for bit (12 x 40 units: helpers active)."""
+    wl = _small("f16", B=12, Hq=40, Hkv=40, S=2048, k=512)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    flags = L.FLAG_SEPARATE_KERNELS if separate else 0
+    H.log(f"concurrent streams separate={separate}")
+    ref_out, ref_idx = _decode_with(L, wl, dev, flags, L.empty_workspace(dev["desc"], wl.d, wl.k))
+    desc = dev["desc"].with_flags(flags)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [L.empty_workspace(dev["desc"], wl.d, wl.k) for _ in streams]
+    torch.cuda.synchronize()
+    results = []
+    for _ in range(6):
+        for s, ws in zip(streams, wss):
+            with torch.cuda.stream(s):
+                idx = torch.full((wl.B, wl.Hq, wl.k), -7, dtype=torch.int32, device="cuda")
+                out = L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc,
+                               idx_out=idx, workspace=ws)
+                results.append((out, idx))
+    torch.cuda.synchronize()
+    for n, (out, idx) in enumerate(results):
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), f"step {n}: index sets differ"
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref_out), f"step {n}: outputs differ"
+
+
 # ------------------------------------------------ dense decode attention
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,S", [("f16", 4, 4, 3000), ("bf16", 8, 2, 1111),
