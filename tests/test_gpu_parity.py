@@ -425,6 +425,12 @@ E2E = {
     "long-11k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=11000, k=1375),
     "long-30k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=30000, k=3000, heavy_frac=0.02),
     "long-40k": dict(dtype="f16", B=1, Hq=1, Hkv=1, S=40000, k=5000),
+    # grouped heads whose selections cover at least half of the tokens
+    # (g*k >= S/2): shared rows, several attention splits per head
+    "gqa2-wide-f16": dict(dtype="f16", B=2, Hq=8, Hkv=4, S=5100, k=1300),
+    "gqa4-wide-900": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=900, k=300),
+    "gqa4-wide-f32": dict(dtype="f32", B=1, Hq=8, Hkv=2, S=4500, k=600, tau=20.0),
+    "gqa4-k-full": dict(dtype="f16", B=1, Hq=4, Hkv=1, S=1500, k=1500),
 }
 
 
@@ -488,6 +494,15 @@ def test_decode_append_end_to_end(L, dtype, separate):
     wl = _small(dtype, S=2600, S_cap=3000, k=333, append=True, heavy_frac=0.02)
     H.log(f"decode_append {dtype} separate={separate}")
     _decode_append_check(L, wl, separate)
+
+
+def test_decode_append_grouped_heads(L):
+    """An appending step of grouped heads on the separate path (g = 4, S above
+    the one-launch limit), with a new key certain to be selected."""
+    wl = _small("bf16", B=2, Hq=8, Hkv=2, S=4500, S_cap=4600, k=600, append=True,
+                heavy_frac=0.02)
+    H.log("decode_append grouped heads")
+    _decode_append_check(L, wl, False, selected=True)
 
 
 # One-launch appends: the new token's score enters the selection in the first
