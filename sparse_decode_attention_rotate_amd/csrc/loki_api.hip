@@ -98,7 +98,8 @@ struct WsLayout {
 WsLayout ws_layout(const Shape& sh, int k) {
   WsLayout w;
   const size_t units = (size_t)sh.B * sh.Hq;
-  w.nsplit = (k + kAttendChunk - 1) / kAttendChunk;
+  // partials for the smaller chunk: either chunk size fits (attend_plan)
+  w.nsplit = (k + kAttendChunkMin - 1) / kAttendChunkMin;
   size_t off = 0;
   w.qr = off;
   off += align256(units * sh.D * 4);
@@ -150,6 +151,16 @@ int compute_units() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Rows per attention workgroup for k rows per query head: 1024 (fewer splits
+// to merge, often none, and fewer workgroups to start) while that still gives
+// a workgroup per compute unit, else 512.  Sets ap.kc and ap.nsplit.
+void attend_plan(AttendParams& ap, const Shape& sh, int k) {
+  const long long rows = (long long)sh.B * sh.Hq;
+  const long long big = rows * ((k + kAttendChunk - 1) / kAttendChunk);
+  ap.kc = big >= compute_units() ? kAttendChunk : kAttendChunkMin;
+  ap.nsplit = (k + ap.kc - 1) / ap.kc;
 }
 
 float scale_log2(const loki_desc* d) {
@@ -297,8 +308,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   ap.part = reinterpret_cast<float*>(ws + w.part);
   ap.k = k;
   ap.d = d;
-  ap.nsplit = w.nsplit;
-  ap.kc = kAttendChunk;
+  attend_plan(ap, sh, ap.k);
   ap.scale_log2 = scale_log2(desc);
   ap.sh = sh;
   return hip_status(launch_attend(ap, st), "attend");
@@ -515,8 +525,7 @@ int loki_attend(const float* qr, const void* kcache, const void* vcache, const i
   ap.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part);
   ap.k = k;
   ap.d = sel_scores ? sh.dp : sh.D;
-  ap.nsplit = w.nsplit;
-  ap.kc = kAttendChunk;
+  attend_plan(ap, sh, ap.k);
   ap.scale_log2 = scale_log2(desc);
   ap.sh = sh;
   return hip_status(launch_attend(ap, (hipStream_t)stream), "attend");
@@ -581,8 +590,7 @@ static int all_tokens_attention(const void* q, const void* kcache, const void* v
   ap.k = sh.S;
   ap.d = d;
   ap.low_dim = low_dim;
-  ap.nsplit = w.nsplit;
-  ap.kc = kAttendChunk;
+  attend_plan(ap, sh, ap.k);
   ap.scale_log2 = scale_log2(desc);
   ap.sh = sh;
   return hip_status(launch_attend(ap, st), what);
