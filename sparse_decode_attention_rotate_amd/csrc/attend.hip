@@ -4,7 +4,7 @@
 // full-dimensional keys of the k selected tokens give the final attention
 // scores; softmax and the value sum run over those k tokens.
 //
-// Workgroup (split, b*Hq+h) stages up to kAttendChunk of the selected token
+// Workgroup (split, b*Hq+h) stages up to p.kc of the selected token
 // indices in LDS and runs block_attend (attend_core.h) over them.  With one
 // split it writes the output row; otherwise it writes (m, l, acc[D]) in the
 // log2 domain and combine_kernel merges the splits.
@@ -27,8 +27,11 @@ constexpr int kXcds = 8;  // MI355X: workgroup i runs on XCD i % 8
 
 template <int DT, int D, bool SPLIT, bool LOW, bool STREAM>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
-  __shared__ int sidx[kAttendChunk];
-  __shared__ float slow[kAttendChunk];
+  // the chunk's index list and partial logits: p.kc entries each (dynamic
+  // LDS sized by the launch, so that small chunks keep small workgroups)
+  extern __shared__ __align__(16) unsigned char att_lists[];
+  int* sidx = reinterpret_cast<int*>(att_lists);
+  float* slow = reinterpret_cast<float*>(att_lists + (size_t)p.kc * 4);
   __shared__ AttendSmem<DT, D, kAttThreads> sm;
 
   const Shape& sh = p.sh;
@@ -159,21 +162,22 @@ hipError_t launch_d(const AttendParams& p, hipStream_t st) {
   // keeps the default policy, so that the g heads reading each chunk share it
   // in L2.
   const bool once = p.sh.g == 1 || p.idx != nullptr;
+  const size_t lists = (size_t)p.kc * 8;  // sidx + slow
   if (p.sel_scores) {
     if (once)
-      attend_kernel<DT, D, true, false, true><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, true, false, true><<<grid, kAttThreads, lists, st>>>(p);
     else
-      attend_kernel<DT, D, true, false, false><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, true, false, false><<<grid, kAttThreads, lists, st>>>(p);
   } else if (p.low_dim) {
     if (once)
-      attend_kernel<DT, D, false, true, true><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, false, true, true><<<grid, kAttThreads, lists, st>>>(p);
     else
-      attend_kernel<DT, D, false, true, false><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, false, true, false><<<grid, kAttThreads, lists, st>>>(p);
   } else {
     if (once)
-      attend_kernel<DT, D, false, false, true><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, false, false, true><<<grid, kAttThreads, lists, st>>>(p);
     else
-      attend_kernel<DT, D, false, false, false><<<grid, kAttThreads, 0, st>>>(p);
+      attend_kernel<DT, D, false, false, false><<<grid, kAttThreads, lists, st>>>(p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;

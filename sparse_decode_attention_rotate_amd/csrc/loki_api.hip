@@ -153,13 +153,24 @@ int compute_units() {
   return cache[dev];
 }
 
-// Rows per attention workgroup for k rows per query head: 1024 (fewer splits
-// to merge, often none, and fewer workgroups to start) while that still gives
-// a workgroup per compute unit, else 512.  Sets ap.kc and ap.nsplit.
+// Rows per attention workgroup (512, 1024 or 2048) for k rows per query
+// head.  One split -- no merge launch -- when the rows alone give a workgroup
+// per compute unit; else the largest chunk that still gives two per compute
+// unit (fewer splits to merge, fewer workgroups to start); else 512.  Sets
+// ap.kc and ap.nsplit.
 void attend_plan(AttendParams& ap, const Shape& sh, int k) {
   const long long rows = (long long)sh.B * sh.Hq;
-  const long long big = rows * ((k + kAttendChunk - 1) / kAttendChunk);
-  ap.kc = big >= compute_units() ? kAttendChunk : kAttendChunkMin;
+  const int cu = compute_units();
+  ap.kc = kAttendChunkMin;
+  if (k <= kAttendChunk && rows >= cu) {
+    while (ap.kc < k) ap.kc *= 2;
+  } else {
+    for (int c = kAttendChunk; c > kAttendChunkMin; c /= 2)
+      if (rows * ((k + c - 1) / c) >= 2LL * cu) {
+        ap.kc = c;
+        break;
+      }
+  }
   ap.nsplit = (k + ap.kc - 1) / ap.kc;
 }
 

@@ -135,7 +135,7 @@ bool fused_supported(const Shape& sh, int d, int k);
 hipError_t launch_fused(const FusedParams& p, hipStream_t st);
 
 // Rows of the selected set processed by one attention workgroup.
-constexpr int kAttendChunk = 1024;    // most rows of one attention workgroup (its LDS lists)
-constexpr int kAttendChunkMin = 512;  // rows per workgroup when 1024 would leave CUs idle
+constexpr int kAttendChunk = 2048;    // most rows of one attention workgroup
+constexpr int kAttendChunkMin = 512;  // fewest (when larger chunks would leave CUs idle)
 
 }  // namespace loki
