@@ -431,6 +431,11 @@ E2E = {
     "gqa4-wide-900": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=900, k=300),
     "gqa4-wide-f32": dict(dtype="f32", B=1, Hq=8, Hkv=2, S=4500, k=600, tau=20.0),
     "gqa4-k-full": dict(dtype="f16", B=1, Hq=4, Hkv=1, S=1500, k=1500),
+    # 256 query rows (a workgroup per compute unit): the separate path's
+    # attention takes each row's k selected tokens in one split of 1024 or
+    # 2048 rows (ragged), with no merge
+    "rows256-k900": dict(dtype="f16", B=8, Hq=32, Hkv=32, S=2000, k=900),
+    "rows256-k1500": dict(dtype="bf16", B=8, Hq=32, Hkv=32, S=2600, k=1500),
 }
 
 
