@@ -239,8 +239,9 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
  * over vanilla attention): qr = q . P[kv], z_t = scale * qr . krot_t over all
  * D coordinates of every token t < S, out = softmax(z) . V.  Because P is
  * orthonormal, qr . krot_t = q . k_t: this is ordinary full attention, read
- * from the same rotated cache.  out [B, Hq, D] in desc->out_dtype.  Split over chunks of
- * the sequence; partial softmax states are merged by a second launch.
+ * from the same rotated cache.  out [B, Hq, D] in desc->out_dtype.  The sequence is
+ * taken in chunks of 512 to 2048 tokens, one workgroup each; when a row has
+ * several chunks their partial softmax states are merged by a second launch.
  * Needs loki_workspace_bytes(desc, D, seq_len) bytes of workspace.
  */
 int loki_full_attention(const void* q, const void* kcache, const void* vcache, const float* P,
