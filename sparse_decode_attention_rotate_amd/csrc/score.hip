@@ -30,7 +30,9 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreBatch = 8;  // 16-byte loads per lane per batch; two batches in flight
-constexpr int kStageScores = 4096;  // scores of one tile staged in LDS (all g heads)
+// scores of one tile staged in LDS (all g heads): groups of four heads take
+// 2048-token tiles (one round of workgroups at the grouped-query shapes)
+constexpr int stage_scores(int g) { return g == 4 ? 8192 : 4096; }
 
 // Tiles whose scores go through LDS: four lanes per token, g in {1, 2, 4}.
 template <int LPT, int G>
@@ -41,7 +43,7 @@ template <int DT, int LPT, int G, bool ROT>
 __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams p) {
   constexpr bool STAGE = kStaged<LPT, G>;
   static_assert(!ROT || STAGE, "the rotating variant is a staged one");
-  __shared__ __align__(16) float stage[STAGE ? kStageScores : 1];  // [G][tile_tokens]
+  __shared__ __align__(16) float stage[STAGE ? stage_scores(G) : 1];  // [G][tile_tokens]
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int TPP = kScoreThreads / LPT;  // tokens per pass
   constexpr int NB = kScoreBatch;
@@ -75,7 +77,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
   constexpr int NQL = DP / 4, RSL = kScoreThreads / NQL, NL = RD / RSL;
   constexpr int NXV = ROT ? ((G + 1) * RD + kScoreThreads - 1) / kScoreThreads : 1;
   __shared__ float xq[ROT ? G + 1 : 1][RD];          // query rows, then the new key
-  __shared__ float qpart[ROT ? NW : 1][ROT ? G + 1 : 1][RD];
+  // per-wave partial sums of the rotation: they live in the stage, which
+  // holds no scores before the stream starts or after the tile is written
+  static_assert(!ROT || NW * (G + 1) * RD <= stage_scores(G), "partials fit the stage");
+  auto qpart = reinterpret_cast<float (*)[G + 1][RD]>(stage);
   __shared__ float qs[ROT ? G : 1][DP];
   __shared__ float kn[ROT ? DP : 1];                  // new key's panel coordinates as stored
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query row of the group
@@ -274,6 +279,44 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
     consume(xb, pass + NB);
     if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
   }
+  if constexpr (STAGE) {
+    __syncthreads();  // every stream store of this tile's scores is in LDS
+    if constexpr (ROT) {
+      if (last) {
+        // the new token's score from its stored panel coordinates (the
+        // stream read the row before this kernel's store may have landed):
+        // lane (h, cl) of wave 0 forms the partial over [cl*E, cl*E + E),
+        // group_sum adds the four partials pairwise (the stream's
+        // reduce-scatter adds the same pairs)
+        if (wave == 0) {
+          const int h = min(lane / LPT, G - 1), cl = lane % LPT;
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; e++) {
+            const int j = cl * E + e;
+            acc = fmaf(j < p.d ? qs[h][j] : 0.f, kn[j], acc);
+          }
+          acc = group_sum<LPT>(acc);
+          if (lane < G * LPT && cl == 0) stage[h * p.tile_tokens + (sh.S - 1 - t0)] = acc;
+        }
+        __syncthreads();
+      }
+    }
+    // the tile's scores, head by head: 16-byte stores where the row allows
+    // (t0 is a multiple of the pass step, so it is 16-byte aligned when S is
+    // a multiple of 4), scalar stores for the rest
+    const int n = t_end - t0;
+    const int n4 = (sh.S % 4 == 0) ? n / 4 * 4 : 0;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float* dst = srow + (size_t)h * sh.S + t0;
+      const float* src = stage + h * p.tile_tokens;
+      for (int e = threadIdx.x * 4; e < n4; e += kScoreThreads * 4)
+        *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
+      for (int e = n4 + threadIdx.x; e < n; e += kScoreThreads) dst[e] = src[e];
+    }
+    if constexpr (ROT) __syncthreads();  // the stage is read out: the partials may reuse it
+  }
   if constexpr (ROT) {
     if (last) {
       // the rest of the new key's row and its value row
@@ -298,7 +341,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       if (lane < 32 && cqr < NQR)
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) qpart[wave][G][DP + 4 * cqr + cc] = ak[cc];
-      __syncthreads();  // also: every stream store of this tile's scores is in LDS
+      __syncthreads();
       for (int j = DP + tid; j < RD; j += kScoreThreads) {
         float s = 0.f;
 #pragma unroll
@@ -309,20 +352,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       for (int j = tid; j < RD; j += kScoreThreads)
         copy_elem<DT>(p.vcache_w, (head * sh.S_cap + (size_t)(sh.S - 1)) * RD + j, p.v_new,
                       head * RD + j);
-      // the new token's score from its stored panel coordinates: lane (h, cl)
-      // of wave 0 forms the partial over [cl*E, cl*E + E), group_sum adds the
-      // four partials pairwise (the stream's reduce-scatter adds the same pairs)
-      if (wave == 0) {
-        const int h = min(lane / LPT, G - 1), cl = lane % LPT;
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-          const int j = cl * E + e;
-          acc = fmaf(j < p.d ? qs[h][j] : 0.f, kn[j], acc);
-        }
-        acc = group_sum<LPT>(acc);
-        if (lane < G * LPT && cl == 0) stage[h * p.tile_tokens + (sh.S - 1 - t0)] = acc;
-      }
     }
     // the first tile of each (b, kv): the remaining coordinates,
     // qs[h][DP:RD] = q[h] . P[kv][:, DP:RD] (32 quad slots x 8 row slots), and
@@ -376,22 +405,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_panel_kernel(ScoreParams 
       }
     }
   }
-  if constexpr (STAGE) {
-    // the tile's scores, head by head: 16-byte stores where the row allows
-    // (t0 is a multiple of the pass step, so it is 16-byte aligned when S is
-    // a multiple of 4), scalar stores for the rest
-    __syncthreads();
-    const int n = t_end - t0;
-    const int n4 = (sh.S % 4 == 0) ? n / 4 * 4 : 0;
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-      float* dst = srow + (size_t)h * sh.S + t0;
-      const float* src = stage + h * p.tile_tokens;
-      for (int e = threadIdx.x * 4; e < n4; e += kScoreThreads * 4)
-        *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src + e);
-      for (int e = n4 + threadIdx.x; e < n; e += kScoreThreads) dst[e] = src[e];
-    }
-  }
 }
 
 // Any d (including d > dp): one thread per token, element loads.
@@ -421,9 +434,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
 int tile_tokens(const Shape& sh, int lpt) {
   const int step = (kScoreThreads / lpt) * 2 * kScoreBatch;
   const long long units = (long long)sh.B * sh.Hkv;
-  long long want = (long long)sh.S * units / (sh.g > 1 ? 2048 : 512);
+  long long want = (long long)sh.S * units / (sh.g > 1 ? 1024 : 512);
   const bool staged = lpt == 4 && (sh.g == 1 || sh.g == 2 || sh.g == 4);
-  const long long cap = staged ? kStageScores / sh.g : 4096;
+  const long long cap = staged ? stage_scores(sh.g) / sh.g : 4096;
   want = want < step ? step : (want > cap ? cap : want);
   return (int)((want + step - 1) / step * step);
 }
