@@ -41,25 +41,35 @@ namespace loki {
 constexpr int kBins = 2048;
 constexpr int kFewCandidates = 64;
 
-__device__ __forceinline__ unsigned order_key(float s) {
-  unsigned u = __float_as_uint(s);
+__host__ __device__ __forceinline__ unsigned order_key(float s) {
+  unsigned u = __builtin_bit_cast(unsigned, s);
   if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Inverse of order_key (a -0 score comes back as +0).
-__device__ __forceinline__ float key_score(unsigned key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+__host__ __device__ __forceinline__ float key_score(unsigned key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-__device__ __forceinline__ int lin_bin(float s, float lo, float scale) {
-  const int b = (int)((s - lo) * scale);
-  return b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
+// Linear bin of score s: floor((s - lo) * scale) clamped to [0, kBins - 1].
+// The clamping is done in float, before the conversion to int, so the bin is
+// defined for every s, lo and scale, and it never decreases as order_key(s)
+// grows: a product at or above kBins - 1 (+inf included) takes the top bin,
+// one at or below 0 (-inf included) bin 0; scale 0 puts every score in bin 0;
+// a NaN score goes where its order key ranks it: the top bin when its sign
+// bit is clear (above +inf), bin 0 when it is set (below -inf).
+__host__ __device__ __forceinline__ int lin_bin(float s, float lo, float scale) {
+  const float x = (s - lo) * scale;
+  if (x >= (float)(kBins - 1)) return kBins - 1;
+  if (x > 0.f) return (int)x;  // 0 < x < kBins - 1: an exact floor
+  if (x == x || scale == 0.f) return 0;
+  return (__builtin_bit_cast(unsigned, s) & 0x80000000u) ? 0 : kBins - 1;
 }
 
 // scale of the linear binning of [lo, hi]; 0 (one bin) when the range is empty,
 // not finite or too small to scale
-__device__ __forceinline__ float bin_scale(float lo, float hi) {
+__host__ __device__ __forceinline__ float bin_scale(float lo, float hi) {
   const float range = hi - lo;
   float scale = (range > 0.f && range < INFINITY) ? (float)(kBins - 1) / range : 0.f;
   return scale < INFINITY ? scale : 0.f;

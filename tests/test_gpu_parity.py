@@ -454,6 +454,29 @@ def test_decode_end_to_end(L, case, separate):
     H.log(f"  {res}")
 
 
+@pytest.mark.parametrize("dtype,B,nh,S,k", [("f16", 2, 4, 3000, 300), ("bf16", 8, 40, 2000, 300)],
+                         ids=["512-threads", "256-threads-helpers"])
+def test_provisional_range_far_from_later_scores(L, dtype, B, nh, S, k):
+    """The one-launch kernel bins every score with a range taken from its first
+    batch of scores.  Here the first 1100 tokens score almost alike (a range
+    thousands of times narrower than the rest) and every later token scores
+    up to a thousand times further out, on both sides: the clamped binning
+    must stay monotone, and the selection exact up to the tie band."""
+    wl = _small(dtype, B=B, Hq=nh, Hkv=nh, S=S, k=k)
+    x = W.generate(wl)
+    K = W.from_storage(x["krot"], dtype)
+    g = np.random.default_rng(17)
+    K[:, :, :1100, :32] = K[:, :, :1, :32] * (1.0 + 1e-3 * g.standard_normal((B, nh, 1100, 1)))
+    K[:, :, 1100:S, :32] *= g.choice([1.0, 30.0, 1000.0], size=(B, nh, S - 1100, 1))
+    x["krot"] = W.to_storage(K, dtype)
+    dev = H.upload(wl, x)
+    assert L.decode_plan(dev["desc"], wl.d, wl.k)
+    H.log(f"provisional binning range {dtype} B={B} heads={nh}")
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {res}")
+
+
 def test_launch_plan(L):
     """Which workloads take the one-launch kernel."""
     expect = {"single_head_f32": True, "llama2_7b_f16": True, "llama2_13b_f16": True,
