@@ -30,7 +30,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-METRIC = "Loki decode-attn µs/step & achieved HBM GB/s (% peak), Llama2-13B shape"
+# the shape each workload stands for, in the metric's label
+SHAPE_LABEL = {"llama2_13b_f16": "Llama2-13B shape", "llama2_7b_f16": "Llama2-7B shape",
+               "single_head_f32": "single head, S=1024, fp32",
+               "long_context_bf16": "long context S=32768 with append, bf16",
+               "gqa_llama3_8b_bf16": "GQA Llama-3-8B shape, bf16"}
+
+
+def metric_label(name):
+    return ("Loki decode-attn µs/step & achieved HBM GB/s (% peak), "
+            + SHAPE_LABEL.get(name, name))
 KERNEL_SOURCES = {"score": "score.hip", "attend": "attend.hip", "topk": "topk.hip",
                   "rotate_query": "project.hip", "fused": "fused.hip"}
 KERNEL_NAMES = {"score": "score_panel_kernel", "attend": "attend_kernel", "topk": "topk_kernel",
@@ -53,6 +62,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only --workload (by default every workload is timed too and "
+                         "reported under \"workloads\")")
+    ap.add_argument("--parity-units", type=int, default=64,
+                    help="(batch, head) units of each other workload checked against the oracle")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after the run, 5 plain device-to-device copies of MB megabytes "
                          "(reference for the HBM byte counters of a profiler run)")
@@ -424,7 +438,7 @@ def main():
 
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
-        "metric": METRIC,
+        "metric": metric_label(wl.name),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -467,6 +481,23 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, gpu)
 
+    if not args.no_workloads:
+        # every workload's step, timed the same way (the default one from the
+        # figures above); the others after it, one at a time
+        del x
+        par = result.get("cpu_baseline", {}).get("parity")
+        idx_h = gpu["idx"] if gpu is not None else None
+        entries = {}
+        for name in W.WORKLOADS:
+            if name == wl.name:
+                if idx_h is None:
+                    continue
+                entries[name] = time_workload(
+                    name, args, headline=(ms_per_step * 1e3, spread, full_us, par, idx_h))
+            else:
+                entries[name] = time_workload(name, args)
+        result["workloads"] = entries
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -477,6 +508,224 @@ def main():
         result["copy_calibration_bytes"] = n
 
     print(json.dumps(result), flush=True)
+
+
+def unit_sample(n_units, n_max):
+    """Up to n_max (batch, head) units spread evenly over the step."""
+    import numpy as np
+    if n_units <= n_max:
+        return list(range(n_units))
+    return sorted(set(np.linspace(0, n_units - 1, n_max).round().astype(int).tolist()))
+
+
+def parity_check(wl, x, out, idx, heads):
+    """The sampled units of a GPU step against the oracle: index sets within
+    the tie band of the oracle's fp64 scores, outputs against the oracle's
+    attention over the GPU's own sets (normwise per row, and elementwise with
+    a floor of 1e-3 of the row's largest magnitude)."""
+    import numpy as np
+    from oracle import loki_oracle as oracle
+
+    krot, v = x["krot"][:, :, :wl.S], x["v"][:, :, :wl.S]
+    if wl.append:  # the cache after the step's own append (the oracle's rotation)
+        kr, vr = oracle.append_rows(x["k_new"], x["v_new"], x["P"], wl.dtype)
+        krot, v = krot.copy(), v.copy()
+        krot[:, :, wl.S - 1] = kr
+        v[:, :, wl.S - 1] = vr
+    r = oracle.decode(x["q"], krot, v, x["P"], wl.d, wl.k, wl.dtype, heads=heads)
+    Hq = wl.Hq
+    swaps = band_ok = 0
+    for u in heads:
+        b, h = divmod(u, Hq)
+        gi = idx[b, h]
+        sc = r["scores"][b, h]
+        ok = (len(np.unique(gi)) == wl.k and gi.min() >= 0 and gi.max() < wl.S and
+              bool(np.all(np.diff(gi) > 0)))
+        if ok and wl.k < wl.S:
+            srt = np.sort(sc)[::-1]
+            tau = 1e-3 * max(abs(srt[wl.k - 1]), 1e-3 * np.abs(sc).max())
+            mask = np.zeros(wl.S, bool)
+            mask[gi] = True
+            ok = sc[mask].min() >= sc[~mask].max() - tau
+            swaps += wl.k - len(np.intersect1d(gi, r["idx"][b, h]))
+        band_ok += int(ok)
+    ref = oracle.attend_given(x["q"], krot, v, x["P"], idx, wl.dtype, heads=heads)
+    errs, elem = [], []
+    for u in heads:
+        b, h = divmod(u, Hq)
+        g_, r_ = out[b, h], ref[b, h]
+        top = max(np.abs(r_).max(), 1e-30)
+        errs.append(np.abs(g_ - r_).max() / top)
+        elem.append((np.abs(g_ - r_) / np.maximum(np.abs(r_), 1e-3 * top)).max())
+    tol = OUT_TOL[wl.dtype]
+    return {"units": len(heads), "index_sets_within_tie_band": band_ok,
+            "swapped_tokens_within_band": int(swaps),
+            "max_rel_out": float(f"{max(errs):.3e}"),
+            "max_rel_out_elementwise_floor": float(f"{max(elem):.3e}"),
+            "tolerance": tol, "ok": bool(band_ok == len(heads) and max(errs) < tol)}
+
+
+def gather_rows(wl, idx):
+    """Rows the attention of one step gathers: per (b, kv) the distinct
+    tokens selected by its query heads (the union), and the nominal count
+    (k per query head)."""
+    import numpy as np
+    g = wl.Hq // wl.Hkv
+    union = 0
+    for b in range(wl.B):
+        for kv in range(wl.Hkv):
+            union += np.unique(idx[b, kv * g:(kv + 1) * g]).size
+    return union, wl.B * wl.Hq * wl.k
+
+
+def time_workload(name, args, headline=None):
+    """One workload's decode step timed as the headline is (cycled cache
+    copies, settle, warm-up, K steps between events on the launch stream,
+    two more regions for the spread), the dense attention over all S tokens on
+    the same caches, and the step checked against the oracle on sampled units.
+    With `headline` (the already measured figures of the default workload)
+    only the entry is assembled."""
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_rotate_amd as loki
+    import workloads as W
+
+    wl = W.get(name)
+    es = 4 if wl.dtype == "f32" else 2
+    score_bytes = es * wl.B * wl.Hkv * wl.S * wl.d
+    desc = loki.Desc(batch=wl.B, n_q_heads=wl.Hq, n_kv_heads=wl.Hkv, head_dim=wl.D,
+                     seq_len=wl.S, seq_capacity=wl.capacity, panel_dim=wl.d,
+                     dtype=loki.NAME_CODE[wl.dtype])
+    plan = "one kernel" if loki.decode_plan(desc, wl.d, wl.k, wl.append) else "separate kernels"
+    if headline is not None:
+        us, spread, dense_us, par, idx_h = headline
+        sets_n = args.sets
+    else:
+        dev = torch.device("cuda:0")
+        t0 = time.time()
+        x = W.generate(wl)
+
+        def up(a):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                    torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        kc0 = loki.empty_kcache(desc)
+        loki.pack_kcache(up(x["krot"]), kc0, desc.with_seq_len(wl.capacity))
+        v0 = up(x["v"])
+        step_bytes = wl.algorithmic_bytes()
+        sets_n = max(3, 1 + -(-(512 << 20) // step_bytes)) if step_bytes >= (32 << 20) else 3
+        sets = [(kc0, v0)] + [(kc0.clone(), v0.clone()) for _ in range(sets_n - 1)]
+        q, P = up(x["q"]), torch.from_numpy(np.ascontiguousarray(x["P"])).to(dev)
+        out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+        idx = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device=dev)
+        ws = loki.empty_workspace(desc, wl.d, wl.k)
+        k_new = up(x["k_new"]) if wl.append else None
+        v_new = up(x["v_new"]) if wl.append else None
+        stream = torch.cuda.current_stream()
+        st = ctypes.c_void_p(stream.cuda_stream)
+        vp = ctypes.c_void_p
+        cd = desc.c()
+        calls = []
+        for kc, vc in sets:
+            if wl.append:
+                calls.append((loki.lib.loki_decode_append,
+                              [vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
+                               vp(kc.data_ptr()), vp(vc.data_ptr()), vp(P.data_ptr()), wl.d,
+                               wl.k, vp(out.data_ptr()), None, None, ctypes.byref(cd),
+                               vp(ws.data_ptr()), ws.numel(), st]))
+            else:
+                calls.append((loki.lib.loki_decode,
+                              [vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                               vp(P.data_ptr()), wl.d, wl.k, vp(out.data_ptr()), None, None,
+                               ctypes.byref(cd), vp(ws.data_ptr()), ws.numel(), st]))
+
+        def step(i):
+            fn, a = calls[i % len(calls)]
+            rc = fn(*a)
+            if rc != 0:
+                raise RuntimeError(f"{name}: {loki.strerror(rc)} {loki.last_error()}")
+
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+
+        def region(fn, n):
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for i in range(n):
+                fn(i)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / n * 1e3
+
+        t_settle = time.time()
+        i = 0
+        while time.time() - t_settle < args.settle:
+            for _ in range(50):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step(i)
+        us = region(step, args.steps)
+        more = sorted([us] + [region(step, args.steps) for _ in range(2)])
+        spread = {"regions": 3, "median_us": round(more[1], 2), "min_us": round(more[0], 2),
+                  "max_us": round(more[2], 2)}
+        # dense attention over all S tokens on the same caches (the pages'
+        # baseline of the Loki speed-up)
+        ws_full = loki.empty_workspace(desc, wl.D, wl.S)
+        wsf, nf = vp(ws_full.data_ptr()), ws_full.numel()
+
+        def dense(i):
+            kc, vc = sets[i % len(sets)]
+            rc = loki.lib.loki_full_attention(vp(q.data_ptr()), vp(kc.data_ptr()),
+                                              vp(vc.data_ptr()), vp(P.data_ptr()),
+                                              vp(out.data_ptr()), ctypes.byref(cd), wsf, nf, st)
+            if rc != 0:
+                raise RuntimeError(f"{name} dense: {loki.last_error()}")
+
+        for i in range(min(args.warmup, 5)):
+            dense(i)
+        dense_us = region(dense, max(10, args.steps // 4))
+        del ws_full
+        # the step once more on copy 0 with its index sets, for the oracle
+        fn, a = calls[0]
+        a = list(a)
+        a[9 if wl.append else 7] = vp(idx.data_ptr())
+        if fn(*a) != 0:
+            raise RuntimeError(f"{name}: {loki.last_error()}")
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy().astype(np.float64)
+        idx_h = idx.cpu().numpy()
+        del sets, kc0, v0, q, P, out, idx, ws, k_new, v_new, calls
+        torch.cuda.empty_cache()
+        heads = unit_sample(wl.B * wl.Hq, args.parity_units)
+        par = parity_check(wl, x, out_h, idx_h, heads)
+        print(f"[bench] {name}: {us:.2f} us/step, parity {par['ok']} "
+              f"({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+        del x
+    nominal_bytes = wl.algorithmic_bytes()
+    entry = {"metric": metric_label(name), "config": W.describe(wl),
+             "launch_plan": plan, "us_per_step": round(us, 2), "spread": spread,
+             "cache_copies_cycled": sets_n}
+    union_rows, nominal_rows = gather_rows(wl, idx_h)
+    if wl.Hq != wl.Hkv:
+        # the gather counts each distinct selected row of a KV group once
+        alg = score_bytes + es * union_rows * 2 * wl.D
+        entry["alg_bytes_union"] = alg
+        entry["alg_bytes_nominal"] = nominal_bytes
+        entry["union_rows_over_nominal"] = round(union_rows / nominal_rows, 4)
+    else:
+        alg = nominal_bytes
+        entry["alg_bytes"] = alg
+    gbs = alg / (us * 1e-6) / 1e9
+    entry.update({"GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                  "target_us_at_70pct": round(alg / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6, 2),
+                  "dense_attention_us": round(dense_us, 2),
+                  "loki_speedup_vs_dense": round(dense_us / us, 3), "parity": par})
+    return entry
 
 
 def cpu_model():
@@ -556,32 +805,7 @@ def cpu_baseline(wl, x, budget_s, gpu=None):
                              "units": n1, "seconds": round(s1, 3)}
     if gpu is not None:
         # the sampled units of the GPU's step against the oracle
-        B, Hq = wl.B, wl.Hq
-        swaps = band_ok = 0
-        for u in heads:
-            b, h = divmod(u, Hq)
-            gi = gpu["idx"][b, h]
-            sc = r["scores"][b, h]
-            ok = (len(np.unique(gi)) == wl.k and gi.min() >= 0 and gi.max() < wl.S and
-                  bool(np.all(np.diff(gi) > 0)))
-            if ok and wl.k < wl.S:
-                srt = np.sort(sc)[::-1]
-                tau = 1e-3 * max(abs(srt[wl.k - 1]), 1e-3 * np.abs(sc).max())
-                mask = np.zeros(wl.S, bool)
-                mask[gi] = True
-                ok = sc[mask].min() >= sc[~mask].max() - tau
-                swaps += wl.k - len(np.intersect1d(gi, r["idx"][b, h]))
-            band_ok += int(ok)
-        ref = oracle.attend_given(x["q"], krot, v, x["P"], gpu["idx"], wl.dtype, heads=heads)
-        errs = []
-        for u in heads:
-            b, h = divmod(u, Hq)
-            errs.append(np.abs(gpu["out"][b, h] - ref[b, h]).max() /
-                        max(np.abs(ref[b, h]).max(), 1e-30))
-        res["parity"] = {"units": n, "index_sets_within_tie_band": band_ok,
-                         "swapped_tokens_within_band": int(swaps),
-                         "max_rel_out": float(f"{max(errs):.3e}"), "tolerance": OUT_TOL[wl.dtype],
-                         "ok": bool(band_ok == n and max(errs) < OUT_TOL[wl.dtype])}
+        res["parity"] = parity_check(wl, x, gpu["out"], gpu["idx"], heads)
     return res
 
 

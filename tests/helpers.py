@@ -10,7 +10,9 @@ Parity rules
     near-ties may swap only inside that band.
   * outputs: the oracle recomputes the attention on the GPU's own index sets;
     per (batch, head) the normwise relative error max|g - r| / max|r| must be
-    below 1e-5 for fp32 storage and 2e-3 for fp16 / bf16 storage.
+    below 1e-5 for fp32 storage and 2e-3 for fp16 / bf16 storage.  The
+    elementwise error with a floor, max |g - r| / max(|r|, 1e-3 max|r|), is
+    reported beside it.
 """
 import numpy as np
 import torch
@@ -134,6 +136,13 @@ def rel_err_rows(g: np.ndarray, r: np.ndarray) -> np.ndarray:
     return num / np.maximum(den, 1e-30)
 
 
+def rel_err_elementwise(g: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Per (b, h) elementwise relative error with a floor: max over the row of
+    |g-r| / max(|r|, 1e-3 * max|r|) (reported beside the normwise error)."""
+    top = np.maximum(np.abs(r).max(axis=-1, keepdims=True), 1e-30)
+    return (np.abs(g - r) / np.maximum(np.abs(r), 1e-3 * top)).max(axis=-1)
+
+
 def full_parity(wl: W.Workload, x: dict, out_gpu, idx_gpu, d=None, k=None, heads=None):
     """End-to-end check; returns a dict of the achieved numbers."""
     d = wl.d if d is None else d
@@ -146,11 +155,13 @@ def full_parity(wl: W.Workload, x: dict, out_gpu, idx_gpu, d=None, k=None, heads
     ref = oracle.attend_given(x["q"], krot, v, x["P"], idx_gpu, wl.dtype, heads=heads)
     if heads is None:
         err = rel_err_rows(out_gpu, ref)
+        elem = rel_err_elementwise(out_gpu, ref)
     else:
-        err = np.array([rel_err_rows(out_gpu[divmod(int(u), wl.Hq)], ref[divmod(int(u), wl.Hq)])
-                        for u in heads])
+        rows = [divmod(int(u), wl.Hq) for u in heads]
+        err = np.array([rel_err_rows(out_gpu[bh], ref[bh]) for bh in rows])
+        elem = np.array([rel_err_elementwise(out_gpu[bh], ref[bh]) for bh in rows])
     if heads is None:
         assert np.all(np.isfinite(out_gpu))
     assert err.max() < OUT_TOL[wl.dtype], f"max rel err {err.max():.3e}"
     return {"rows": n, "rows_with_band_swaps": int(n_diff), "swapped_tokens": int(n_swaps),
-            "max_rel_err": float(err.max())}
+            "max_rel_err": float(err.max()), "max_rel_err_elementwise_floor": float(elem.max())}
