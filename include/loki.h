@@ -218,6 +218,25 @@ int loki_decode(const void* q, const void* kcache, const void* vcache, const flo
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): loki_decode
+ * with the workspace taken from a fixed scratch array inside the library
+ * instead of a caller's buffer.  Same arguments, launches and results as
+ * loki_decode, without `workspace` / `workspace_bytes`.  Nothing is allocated
+ * or freed: each GPU the library runs on holds its own copy of the array,
+ * LOKI_NOALLOC_SCRATCH_BYTES bytes, from the first call on that device until
+ * the process ends.  A step whose loki_workspace_bytes(desc, d, k) exceeds
+ * that size is refused with LOKI_EWORKSPACE before anything else is done.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must not be made; use
+ * loki_decode with distinct workspaces for those.
+ */
+#define LOKI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int loki_decode_noalloc(const void* q, const void* kcache, const void* vcache, const float* P,
+                        int d, int k, void* out, int32_t* idx_out, float* scores_out,
+                        const loki_desc* desc, void* stream);
+
+/*
  * Append then decode [C], [F1]: appends (k_new, v_new) at row pos = S-1 as
  * loki_append does, then runs loki_decode over the S tokens (the new one
  * included).  k_new, v_new [B, Hkv, D] storage dtype.  As separate launches

@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 F32, F16, BF16 = 0, 1, 2
 FLAG_SEPARATE_KERNELS = 1
 FLAG_NO_HELPERS = 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LOKI_NOALLOC_SCRATCH_BYTES of include/loki.h
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 NAME_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
@@ -40,7 +41,7 @@ EXPORTS = ["loki_strerror", "loki_last_error", "loki_kcache_elems", "loki_worksp
            "loki_pack_kcache", "loki_unpack_kcache", "loki_append", "loki_rotate_query",
            "loki_score", "loki_topk", "loki_attend", "loki_decode", "loki_decode_append",
            "loki_decode_plan", "loki_full_attention", "loki_prefill", "loki_pca_attention",
-           "loki_calibrate_workspace_bytes", "loki_calibrate"]
+           "loki_calibrate_workspace_bytes", "loki_calibrate", "loki_decode_noalloc"]
 
 
 class _CDesc(ctypes.Structure):
@@ -75,6 +76,7 @@ _SIG = {
     "loki_calibrate_workspace_bytes": ([_D, ctypes.c_int32, ctypes.POINTER(_sz)], _i),
     "loki_calibrate": ([_vp, ctypes.c_int32, _vp, _vp, _D, _vp, _sz, _vp], _i),
     "loki_prefill": ([_vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _D, _vp], _i),
+    "loki_decode_noalloc": ([_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _D, _vp], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(_lib, _name)
@@ -305,6 +307,21 @@ def decode(q, kcache, vcache, P, d: int, k: int, desc: Desc, out=None, idx_out=N
     _check(_lib.loki_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), d, k, _ptr(out),
                             _ptr(idx_out), _ptr(scores_out), ctypes.byref(desc.c()),
                             _ptr(workspace), workspace.numel(), _stream(stream)), "loki_decode")
+    return out
+
+
+def decode_noalloc(q, kcache, vcache, P, d: int, k: int, desc: Desc, out=None, idx_out=None,
+                   stream=None, scores_out=None):
+    """loki_decode_noalloc: one decode step whose workspace is the library's
+    fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES); nothing is allocated
+    beyond `out` when it is not given."""
+    _expect(q, (desc.batch, desc.n_q_heads, desc.head_dim), desc.torch_dtype, "q")
+    _check_decode_outputs(desc, k, idx_out, scores_out)
+    out = _out(desc, out, q.device)
+    _check(_lib.loki_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(P), d, k,
+                                    _ptr(out), _ptr(idx_out), _ptr(scores_out),
+                                    ctypes.byref(desc.c()), _stream(stream)),
+           "loki_decode_noalloc")
     return out
 
 

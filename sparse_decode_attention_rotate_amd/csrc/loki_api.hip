@@ -15,6 +15,13 @@
 
 using namespace loki;
 
+// Scratch of loki_decode_noalloc: device memory in the library's own code
+// object, one copy per GPU, held until the process ends.  Its name is only a
+// host-side stand-in for the array; host code reaches the memory through the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = LOKI_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -325,6 +332,25 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
   return hip_status(launch_attend(ap, st), "attend");
 }
 
+int scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(LOKI_EUNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LOKI_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return LOKI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -556,6 +582,24 @@ int loki_decode_append(const void* q, const void* k_new, const void* v_new, void
                        void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_new, v_new, kcache, vcache, P, d, k, out, idx_out, scores_out, desc,
                      workspace, workspace_bytes, stream, true);
+}
+
+int loki_decode_noalloc(const void* q, const void* kcache, const void* vcache, const float* P,
+                        int d, int k, void* out, int32_t* idx_out, float* scores_out,
+                        const loki_desc* desc, void* stream) {
+  // the size check comes first: an oversized call is refused before any HIP call
+  size_t need = 0;
+  int rc = loki_workspace_bytes(desc, d, k, &need);
+  if (rc) return rc;
+  if (need > kScratchBytes)
+    return fail(LOKI_EWORKSPACE,
+                "loki_decode_noalloc: this step needs %zu bytes of scratch, above the "
+                "library's fixed %zu bytes; use loki_decode with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return decode_impl(q, nullptr, nullptr, const_cast<void*>(kcache), const_cast<void*>(vcache),
+                     P, d, k, out, idx_out, scores_out, desc, ws, kScratchBytes, stream, false);
 }
 
 // Dense (low_dim = 0) or low-dimensional (PCAAttn) attention over all S
