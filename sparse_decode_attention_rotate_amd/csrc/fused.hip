@@ -49,24 +49,6 @@ constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per ba
 constexpr size_t kFusedDynBytes = 36 * 1024;
 constexpr int kFusedRowsPerBatch = 4;  // gather rows per lane group per batch
 
-// Words exchanged between the two workgroups of a paired unit are accessed
-// only with agent-coherent loads and stores (relaxed agent-scope atomics,
-// which bypass the non-coherent caches): a workgroup waits until its stores
-// are complete before it touches the pair's flag, and reads its partner's
-// words only after the flag showed the partner had been there.  No cache
-// writeback or invalidate is needed (release / acquire fences would write
-// back or invalidate a whole L2 each time, at a cost to every workgroup on
-// that die).
-__device__ __forceinline__ void st_coherent(float* a, float v) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(a), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* a) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(a), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
 template <int DT, int D, int LPT, int G, int NT, bool APPEND>
 __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParams p) {
   constexpr int GR = G + (APPEND ? 1 : 0);  // rows rotated: the queries, then the new key
@@ -425,7 +407,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     if (G == 1) {
       auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
       RowView<NT, KREG, decltype(load_score)> row(load_score, S);
-      select_from_histogram<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale);
+      select_from_histogram<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, ssm.whist);
       __syncthreads();
     } else {
       for (int h = 0; h < G; h++) {

@@ -262,6 +262,49 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
     }
     return hip_status(launch_fused(fp, st), "fused");
   }
+  // Longer rows (up to 32768 tokens), or grouped heads whose scores do not
+  // fit one workgroup: the one-launch kernel with one query head per
+  // workgroup and its row of scores in LDS.
+  if (!scores_out && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && head_supported(sh, d, k)) {
+    HeadParams hp{};
+    hp.q = q;
+    hp.k_new = append ? k_new : nullptr;
+    hp.v_new = append ? v_new : nullptr;
+    hp.kcache = kcache;
+    hp.vcache = vcache;
+    hp.P = P;
+    hp.out = out;
+    hp.idx_out = idx_out;
+    hp.k = k;
+    hp.scale_log2 = scale_log2(desc);
+    hp.sh = sh;
+    const int heads = sh.B * sh.Hq;
+    hp.n_heads = heads;
+    if (sh.g == 1) {
+      hp.n_slots = heads;
+      // Paired heads: while the heads leave resident workgroup slots free
+      // (two per compute unit at 512 threads, one at 1024), up to as many
+      // helpers as free slots (a multiple of 8, so that a helper and its
+      // head share one XCD's L2) attend the second half of a head's rows.
+      const int slots = compute_units() * (head_kernel_threads(sh) == 512 ? 2 : 1);
+      int n_help = 0;
+      if (k >= 256 && heads < slots && !(desc->flags & LOKI_FLAG_NO_HELPERS))
+        n_help = (heads < slots - heads ? heads : slots - heads) / 8 * 8;
+      hp.n_help = n_help;
+      hp.help_first = heads - n_help;
+      hp.k0 = (k / 2 + 63) / 64 * 64;
+      if (n_help > 0) {
+        hp.help_part = reinterpret_cast<float*>(ws + w.help_part);
+        hp.help_flag = reinterpret_cast<unsigned long long*>(ws + w.help_flag);
+        hp.tag = next_tag(workspace);
+      }
+    } else {
+      // the g heads of a (b, kv) on one XCD: whole blocks of 8 (b, kv) units
+      hp.n_slots = (sh.B * sh.Hkv + 7) / 8 * 8 * sh.g;
+      hp.help_first = heads;
+    }
+    return hip_status(launch_head(hp, st), "head");
+  }
 
   // For the score kernel's staged tiles (head_dim 128, four lanes per token,
   // 1, 2 or 4 query heads per KV head), the score kernel can rotate the query
@@ -396,7 +439,8 @@ int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_l
   if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
   (void)append;  // the one-launch kernel appends too
-  *one_launch = (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) ? 1 : 0;
+  *one_launch = (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) &&
+                 (fused_supported(sh, d, k) || head_supported(sh, d, k))) ? 1 : 0;
   return LOKI_OK;
 }
 

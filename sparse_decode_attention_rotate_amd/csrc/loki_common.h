@@ -191,6 +191,26 @@ __device__ __forceinline__ int lane_rank(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
 }
 
+// ---------------------------------------------------------------- paired workgroups
+//
+// Words exchanged between the two workgroups of a paired unit are accessed
+// only with agent-coherent loads and stores (relaxed agent-scope atomics,
+// which bypass the non-coherent caches): a workgroup waits until its stores
+// are complete before it touches the pair's flag, and reads its partner's
+// words only after the flag showed the partner had been there.  No cache
+// writeback or invalidate is needed (release / acquire fences would write
+// back or invalidate a whole L2 each time, at a cost to every workgroup on
+// that die).
+__device__ __forceinline__ void st_coherent(float* a, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(a), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* a) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(a), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
 // ---------------------------------------------------------------- K cache layout
 //
 // Split-panel rotated key cache.  Per (batch, KV head) one block of S_cap*D

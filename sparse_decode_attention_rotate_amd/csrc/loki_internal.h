@@ -88,6 +88,28 @@ struct FusedParams {
   Shape sh;
 };
 
+struct HeadParams {
+  const void* q;        // [B,Hq,D]
+  const void* k_new;    // [B,Hkv,D] nullable: appended as token S-1 when set
+  const void* v_new;    // [B,Hkv,D]
+  void* kcache;         // written only at row S-1, when appending
+  void* vcache;
+  const float* P;       // [Hkv,D,D]
+  void* out;            // [B,Hq,D] in sh.odt
+  int32_t* idx_out;     // [B,Hq,k] nullable
+  int k;
+  float scale_log2;
+  int n_slots;          // workgroups of the heads (grouped heads: padded to whole XCD blocks)
+  // paired heads (single query head per KV head): helpers for heads
+  // [help_first, help_first + n_help), workgroups n_heads ...
+  int n_heads;          // B * Hq
+  int help_first, n_help, k0;
+  float* help_part;     // [n_help][2][D + 2] partials (coherent accesses only)
+  unsigned long long* help_flag;  // [n_help] launch tag of the first half done
+  unsigned long long tag;         // unique per launch on one workspace, nonzero
+  Shape sh;
+};
+
 struct PrefillParams {
   const void* k_rows;  // [B, Hkv, n_tokens, D] storage dtype, unrotated keys
   const float* P;      // [Hkv, D, D]
@@ -133,6 +155,13 @@ hipError_t launch_calibrate(const CalibParams& p, hipStream_t st);
 // per-unit scores fit the workgroup's LDS budget.
 bool fused_supported(const Shape& sh, int d, int k);
 hipError_t launch_fused(const FusedParams& p, hipStream_t st);
+
+// One-launch decode step with one query head per workgroup and its whole row
+// of scores in LDS (rows up to 32768 tokens), for shapes the kernel above
+// does not take.
+bool head_supported(const Shape& sh, int d, int k);
+int head_kernel_threads(const Shape& sh);
+hipError_t launch_head(const HeadParams& p, hipStream_t st);
 
 // Rows of the selected set processed by one attention workgroup.
 constexpr int kAttendChunk = 2048;    // most rows of one attention workgroup

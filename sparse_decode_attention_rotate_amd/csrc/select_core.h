@@ -75,7 +75,8 @@ __host__ __device__ __forceinline__ float bin_scale(float lo, float hi) {
   return scale < INFINITY ? scale : 0.f;
 }
 
-// LDS scratch of one selection.
+// LDS scratch of one selection, with the radix passes' per-wave histograms
+// (whist) right after the bin histogram (select_rows keeps its lists in both).
 template <int NW>
 struct SelectSmem {
   unsigned hist[kBins];
@@ -89,11 +90,30 @@ struct SelectSmem {
   unsigned thr_key, r_digit, r_gt, r_eq;
   int thr_idx;
   int wcnt[NW];
+  unsigned key_lo, key_hi1;  // keys of the threshold group: [key_lo, key_hi1]
+};
+
+// The same without whist: for callers that put the per-wave histograms of the
+// radix passes (NW x 256 words, used only after the bin histogram's scans) in
+// LDS they reuse, and pass them to select_from_histogram.
+template <int NW>
+struct SelectSmemLite {
+  unsigned hist[kBins];
+  float wmin[NW], wmax[NW];
+  float wsum[NW], wsq[NW];
+  unsigned wtot[NW];
+  int sel_bin, sel_gt, sel_eq, n_cand;
+  unsigned cand_key[kFewCandidates];
+  int cand_idx[kFewCandidates];
+  unsigned thr_key, r_digit, r_gt, r_eq;
+  int thr_idx;
+  int wcnt[NW];
+  unsigned key_lo, key_hi1;  // keys of the threshold group: [key_lo, key_hi1]
 };
 
 // Zero the histogram (all NT threads; a barrier must follow before use).
-template <int NT, int NW>
-__device__ __forceinline__ void select_clear(SelectSmem<NW>& sm) {
+template <int NT, typename SM>
+__device__ __forceinline__ void select_clear(SM& sm) {
   for (int e = threadIdx.x; e < kBins; e += NT) sm.hist[e] = 0u;
   if (threadIdx.x == 0) sm.n_cand = 0;
 }
@@ -140,8 +160,8 @@ struct RowView {
 // Step 1b: descending scan over the histogram; sets sm.sel_bin (the bin b*
 // holding the k-th largest score), sm.sel_gt (members of higher bins) and
 // sm.sel_eq (members of b*).  All NT threads; ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void select_scan(SelectSmem<NT / 64>& sm, int k) {
+template <int NT, typename SM>
+__device__ __forceinline__ void select_scan(SM& sm, int k) {
   constexpr int NW = NT / 64;
   constexpr int BPL = kBins / NW / 64;  // bins per lane in the scan
   static_assert(BPL >= 1 && kBins % (NW * 64) == 0, "bins split over the waves");
@@ -172,12 +192,16 @@ __device__ __forceinline__ void select_scan(SelectSmem<NT / 64>& sm, int k) {
   __syncthreads();
 }
 
-// Step 2 for a crowded b*: radix passes over 8-bit digits of the keys of
-// b*'s members (per-wave LDS histograms) give (T, I), the last taken element,
-// in sm.thr_key / sm.thr_idx.  All NT threads; ends with a barrier.
-template <int NT, int KREG, typename Load>
-__device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, int bstar, int rem,
-                                                float lo, float scale, SelectSmem<NT / 64>& sm) {
+// Step 2 for a crowded threshold group: radix passes over 8-bit digits of the
+// keys of the group's members (member(key) true; per-wave LDS histograms) give
+// (T, I), the rem-th member in the selection order, in sm.thr_key /
+// sm.thr_idx; whist: NT/64 rows of 256 words of LDS.  All NT threads; ends
+// with a barrier.
+// PADDED: member() is false for every padding element (index >= S), so the
+// index is not checked.
+template <int NT, int KREG, bool PADDED = false, typename Load, typename SM, typename Member>
+__device__ __forceinline__ void radix_threshold_of(RowView<NT, KREG, Load>& row, Member&& member,
+                                                   int rem, SM& sm, unsigned (*whist)[256]) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = row.S;
@@ -187,11 +211,11 @@ __device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, in
   bool whole = false;
   for (int pass = 0; pass < 4; pass++) {
     const int shift = 24 - 8 * pass;
-    for (int e = tid; e < NW * 256; e += NT) (&sm.whist[0][0])[e] = 0u;
+    for (int e = tid; e < NW * 256; e += NT) (&whist[0][0])[e] = 0u;
     __syncthreads();
     row.each([&](int i, unsigned key) {
-      if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
-        atomicAdd(&sm.whist[wave][(key >> shift) & 0xffu], 1u);
+      if ((PADDED || i < S) && member(key) && (key & pmask) == prefix)
+        atomicAdd(&whist[wave][(key >> shift) & 0xffu], 1u);
     });
     __syncthreads();
     if (wave == 0) {
@@ -202,7 +226,7 @@ __device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, in
         const int dg = 255 - (lane * 4 + u);
         unsigned s = 0u;
 #pragma unroll
-        for (int w = 0; w < NW; w++) s += sm.whist[w][dg];
+        for (int w = 0; w < NW; w++) s += whist[w][dg];
         cc[u] = s;
         t4 += s;
       }
@@ -231,7 +255,7 @@ __device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, in
   // whole, else the rr-th one in index order
   unsigned tmin = 0xffffffffu;
   row.each([&](int i, unsigned key) {
-    if (i < S && lin_bin(key_score(key), lo, scale) == bstar && (key & pmask) == prefix)
+    if ((PADDED || i < S) && member(key) && (key & pmask) == prefix)
       tmin = min(tmin, key);
   });
 #pragma unroll
@@ -248,13 +272,13 @@ __device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, in
   } else {
     // the rr-th index (ascending) among keys equal to T
     int cnt = 0;
-    row.each([&](int i, unsigned key) { cnt += __popcll(__ballot(i < S && key == T)); });
+    row.each([&](int i, unsigned key) { cnt += __popcll(__ballot((PADDED || i < S) && key == T)); });
     if (lane == 0) sm.wcnt[wave] = cnt;
     __syncthreads();
     int seen = 0;
     for (int w = 0; w < wave; w++) seen += sm.wcnt[w];
     row.each([&](int i, unsigned key) {
-      const bool eq = i < S && key == T;
+      const bool eq = (PADDED || i < S) && key == T;
       const unsigned long long be = __ballot(eq);
       if (eq && seen + lane_rank(be) == rr - 1) {
         sm.thr_key = T;
@@ -266,13 +290,25 @@ __device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, in
   __syncthreads();
 }
 
+// radix_threshold_of for the members of linear bin bstar.
+template <int NT, int KREG, typename Load, typename SM>
+__device__ __forceinline__ void radix_threshold(RowView<NT, KREG, Load>& row, int bstar, int rem,
+                                                float lo, float scale, SM& sm,
+                                                unsigned (*whist)[256]) {
+  radix_threshold_of<NT, KREG>(
+      row, [&](unsigned key) { return lin_bin(key_score(key), lo, scale) == bstar; }, rem, sm,
+      whist);
+}
+
 // Steps 1 (after the histogram) to 3.  sm.hist holds the histogram of the
-// row under (lo, scale) and sm.n_cand is 0.  All NT threads call it together.
-template <int NT, int KREG, typename Load>
+// row under (lo, scale) and sm.n_cand is 0; whist: the radix passes' per-wave
+// histograms (NT/64 rows of 256 words of LDS; written only when the bin of
+// the k-th score stays crowded).  All NT threads call it together.
+template <int NT, int KREG, typename Load, typename SM>
 __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& row, int k,
                                                       int32_t* out_idx, float* out_val,
-                                                      SelectSmem<NT / 64>& sm, float lo,
-                                                      float scale) {
+                                                      SM& sm, float lo, float scale,
+                                                      unsigned (*whist)[256]) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = row.S;
@@ -363,7 +399,7 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     __syncthreads();
   } else {
-    radix_threshold<NT, KREG>(row, bstar, rem0, lo, scale, sm);
+    radix_threshold<NT, KREG>(row, bstar, rem0, lo, scale, sm, whist);
     const unsigned Tk = sm.thr_key;
     const int Ik = sm.thr_idx;
     int cnt = 0;
@@ -389,6 +425,283 @@ __device__ __forceinline__ void select_from_histogram(RowView<NT, KREG, Load>& r
     }
     out += __popcll(bs);
   });
+}
+
+// The smallest key K in [a, b) (b <= 2^32) for which pred(K) holds, or b
+// when none does; pred must be monotone on [a, b) (false, then true).  One
+// wave searches 64-way: each round its lanes test 64 evenly spaced keys, so a
+// 32-bit range takes six rounds.  Every lane returns the same value.
+template <typename Pred>
+__device__ __forceinline__ unsigned long long first_key_where(unsigned long long a,
+                                                              unsigned long long b, Pred&& pred) {
+  const unsigned long long lane = threadIdx.x & 63;
+  unsigned long long lo = a, hi = b;  // the answer is in [lo, hi]; keys below lo fail
+  while (lo < hi) {
+    const unsigned long long n = hi - lo, step = (n + 63) >> 6;
+    const unsigned long long cand = lo + lane * step;
+    const unsigned long long m = __ballot(cand < hi && pred((unsigned)cand));
+    if (m != 0ull) {
+      const unsigned long long i0 = (unsigned long long)__builtin_ctzll(m);
+      hi = lo + i0 * step;  // pred holds here
+      if (i0 == 0) break;   // and at lo: lo is the answer
+      lo += (i0 - 1) * step + 1;
+    } else {
+      const unsigned long long last = (n - 1) / step < 63 ? (n - 1) / step : 63;
+      lo += last * step + 1;  // every tested key failed
+    }
+  }
+  return hi;
+}
+
+// As first_key_where, but first testing the 64 keys around `guess` (the
+// order key of the score at which pred is expected to turn true): when that
+// window holds the turning point, one round decides; otherwise the search
+// goes on above or below the window.
+template <typename Pred>
+__device__ __forceinline__ unsigned long long first_key_near(unsigned long long a,
+                                                             unsigned long long b, unsigned guess,
+                                                             Pred&& pred) {
+  const unsigned long long lane = threadIdx.x & 63;
+  unsigned long long w0 = guess >= 31u ? (unsigned long long)guess - 31 : 0ull;
+  if (w0 < a) w0 = a;
+  if (w0 >= b) return first_key_where(a, b, pred);
+  const unsigned long long key = w0 + lane;
+  const unsigned long long m = __ballot(key < b && pred((unsigned)key));
+  if (m == 0ull) return first_key_where(w0 + 64 < b ? w0 + 64 : b, b, pred);  // all below
+  if ((m & 1ull) == 0ull || w0 == a) return w0 + (unsigned long long)__builtin_ctzll(m);
+  return first_key_where(a, w0, pred);  // pred holds at w0: the turning point is below
+}
+
+// The smallest key in [a, b) whose linear bin under (lo, scale) is at least
+// target (b when none is): bins are monotone in the key.
+__device__ __forceinline__ unsigned long long first_key_of_bin(unsigned long long a,
+                                                               unsigned long long b, int target,
+                                                               float lo, float scale) {
+  if (target <= 0) return a;
+  if (target >= kBins || scale == 0.f) return b;
+  // the bin's lower edge in score space, a guess within a few ulps
+  const unsigned guess = order_key(lo + (float)target / scale);
+  return first_key_near(a, b, guess, [&](unsigned key) {
+    return lin_bin(key_score(key), lo, scale) >= target;
+  });
+}
+
+// Steps 1 (after the histogram) to 3 for a caller that needs the selected
+// elements but not in index order (the attention over them).  The binning is
+// monotone in the order key, so the members of the bin b* holding the k-th
+// score are the keys of one interval [K_lo, K_hi] and the members of higher
+// bins are the keys above K_hi: after the scan two waves find both ends
+// (first_key_of_bin: one 64-key round near the bin's edge), and every pass
+// over the keys compares integers.
+//  * a crowded b* (more than kFewCandidates members) is split into kBins
+//    linear sub-bins (one pass over the interval's keys and a scan) and the
+//    interval narrowed to the sub-bin holding the k-th score; radix passes
+//    over the interval's keys resolve a group still crowded after that;
+//  * one pass counts, per lane, the keys above the interval and marks the
+//    interval's keys (a bit per key, registers only); the marked candidates
+//    are ranked by (key descending, index ascending) and the rem first are
+//    taken; (T, I) is the last taken;
+//  * one pass writes the taken elements: element i with key > T, or
+//    key == T and i <= I.  Each lane writes its own ones consecutively from
+//    an offset given by the counts of the waves and lanes before it, so the
+//    output is ordered by (wave, lane, element of the lane), not by index;
+//    the order is a function of the keys alone (deterministic).
+// Padding elements (index >= S) must have key 0 (load_score gives them the
+// all-ones NaN) and no score may have those bits: key 0 is then never taken
+// and no pass checks the index.  sm.hist holds the histogram under
+// (lo, scale) and sm.n_cand is 0; lane_extra: NT ints of LDS; whist: the
+// radix passes' per-wave histograms.  Writes k entries of out_idx / out_val
+// (the taken indices and their scores, -0 as +0) and sm.thr_key /
+// sm.thr_idx = (T, I).  All NT threads; the caller needs a barrier before
+// reading the output.
+template <int NT, int KREG, typename Load, typename SM>
+__device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k, int32_t* out_idx,
+                                            float* out_val, SM& sm, float lo, float scale,
+                                            unsigned (*whist)[256], int* lane_extra) {
+  constexpr int NW = NT / 64;
+  static_assert(NW >= 2, "two waves search the interval's ends");
+  static_assert(KREG > 0 && KREG <= 32, "keys in registers, a bit per key of a thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  lane_extra[tid] = 0;
+
+  select_scan<NT>(sm, k);  // ends with a barrier (lane_extra is zero)
+  const int bstar = sm.sel_bin;
+  const int rem0 = k - sm.sel_gt;  // 1 <= rem0 <= members of b*
+  int rem = rem0, nb = sm.sel_eq;
+  // ---- the keys of b*: [K_lo, K_hi); K_hi = 2^32 when b* is the top bin
+  if (wave < 2) {
+    const unsigned long long e = first_key_of_bin(0ull, 1ull << 32, bstar + wave, lo, scale);
+    if (lane == 0) {
+      if (wave == 0)
+        sm.key_lo = (unsigned)e;
+      else
+        sm.key_hi1 = (unsigned)(e - 1);  // K_hi >= 1: key 0 lies in bin 0
+    }
+  }
+  __syncthreads();
+  // key 0 belongs to the padding only
+  unsigned klo = max(sm.key_lo, 1u), khi1 = sm.key_hi1;
+
+  // ---- a crowded b*: linear sub-bins of its interval
+  if (nb > kFewCandidates && scale > 0.f && scale * (float)kBins < INFINITY) {
+    const float lo2 = lo + (float)bstar / scale, scale2 = scale * (float)kBins;
+    for (int e = tid; e < kBins; e += NT) sm.hist[e] = 0u;
+    __syncthreads();  // every thread has read the first scan's results
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      const unsigned key = row.kv[j];
+      if (key >= klo && key <= khi1) atomicAdd(&sm.hist[lin_bin(key_score(key), lo2, scale2)], 1u);
+    }
+    __syncthreads();
+    select_scan<NT>(sm, rem0);
+    const int sub = sm.sel_bin;
+    rem = rem0 - sm.sel_gt;
+    nb = sm.sel_eq;
+    const unsigned long long a = klo, b = (unsigned long long)khi1 + 1;
+    if (wave < 2) {
+      const unsigned long long e = first_key_of_bin(a, b, sub + wave, lo2, scale2);
+      if (lane == 0) {
+        if (wave == 0)
+          sm.key_lo = (unsigned)e;
+        else
+          sm.key_hi1 = (unsigned)(e - 1);  // e > a: the sub-bin has members
+      }
+    }
+    __syncthreads();
+    klo = max(sm.key_lo, 1u);
+    khi1 = sm.key_hi1;
+  }
+
+  // ---- the last taken element (T, I) and each lane's number of taken ones
+  unsigned mine;  // this lane's taken elements, but for taken candidates
+  if (nb <= kFewCandidates) {
+    unsigned gt = 0u, cmask = 0u;
+    const unsigned span = khi1 - klo;  // key - klo <= span: klo <= key <= khi1
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      const unsigned key = row.kv[j];
+      gt += key > khi1 ? 1u : 0u;
+      cmask |= (key - klo <= span) ? (1u << j) : 0u;
+    }
+    mine = gt;
+    if (__ballot(cmask != 0u) != 0ull) {  // rare: this wave holds members of the group
+#pragma unroll
+      for (int j = 0; j < KREG; j++) {
+        if (cmask & (1u << j)) {
+          const int slot = atomicAdd(&sm.n_cand, 1);
+          sm.cand_key[slot] = row.kv[j];
+          sm.cand_idx[slot] = row.base + j * 64;
+        }
+      }
+    }
+    gt = (unsigned)wave_sum((float)gt);  // exact: counts below 2^24
+    if (lane == 0) sm.wcnt[wave] = (int)gt;
+    __syncthreads();
+    // rank of candidate c = members ordered before it by (key descending,
+    // index ascending): one ballot over the candidates on the lanes; the
+    // waves take the candidates in turn; a taken one counts for its wave and
+    // its lane (element i sits on thread (i / per_wave) * 64 + i % 64)
+    {
+      const bool have = lane < nb;
+      const unsigned mk = have ? sm.cand_key[lane] : 0u;
+      const int mi = have ? sm.cand_idx[lane] : INT_MAX;
+      for (int c = wave; c < nb; c += NW) {
+        const unsigned ck = (unsigned)__builtin_amdgcn_readlane((int)mk, c);
+        const int ci = __builtin_amdgcn_readlane(mi, c);
+        const int rank = __popcll(__ballot(have && (mk > ck || (mk == ck && mi < ci))));
+        if (lane == 0) {
+          if (rank == rem - 1) {  // exactly one candidate
+            sm.thr_key = ck;
+            sm.thr_idx = ci;
+          }
+          if (rank < rem) {
+            const int w = ci / row.per_wave;
+            atomicAdd(&sm.wcnt[w], 1);
+            atomicAdd(&lane_extra[w * 64 + ci % 64], 1);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    radix_threshold_of<NT, KREG, true>(
+        row, [&](unsigned key) { return key >= klo && key <= khi1; }, rem, sm, whist);
+    const unsigned T = sm.thr_key;
+    const int I = sm.thr_idx;
+    unsigned cnt = 0u;
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      const unsigned key = row.kv[j];
+      cnt += (key > T || (key == T && row.base + j * 64 <= I)) ? 1u : 0u;
+    }
+    mine = cnt;
+    cnt = (unsigned)wave_sum((float)cnt);
+    if (lane == 0) sm.wcnt[wave] = (int)cnt;
+    __syncthreads();
+  }
+
+  // ---- write the taken elements, each lane its own consecutively
+  const unsigned T = sm.thr_key;
+  const int I = sm.thr_idx;
+  const unsigned own = mine + (unsigned)lane_extra[tid];
+  int out = (int)(wave_incl_scan(own) - own);
+  for (int w = 0; w < wave; w++) out += sm.wcnt[w];
+#pragma unroll
+  for (int j = 0; j < KREG; j++) {
+    const unsigned key = row.kv[j];
+    const int i = row.base + j * 64;
+    if (key > T || (key == T && i <= I)) {
+      out_idx[out] = i;
+      out_val[out] = key_score(key);
+      out++;
+    }
+  }
+}
+
+// The taken elements of select_keys (same keys, same (T, I) in sm) as a
+// bitmap, then their indices in ascending order to `dst` (global memory).
+// bits: S/64 + 1 words of LDS; scan: NT/64 ints of LDS.  All NT threads.
+template <int NT, int KREG, typename Load, typename SM>
+__device__ __forceinline__ void write_taken_in_order(RowView<NT, KREG, Load>& row, SM& sm,
+                                                     unsigned long long* bits, int* scan,
+                                                     int32_t* dst) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned T = sm.thr_key;
+  const int I = sm.thr_idx;
+  // element i = wave * per_wave + j * 64 + lane: word (wave * per_wave) / 64 + j
+  const int words = (row.S + 63) / 64;
+#pragma unroll
+  for (int j = 0; j < KREG; j++) {
+    const unsigned key = row.kv[j];
+    const int i = row.base + j * 64;
+    const unsigned long long m = __ballot(key > T || (key == T && i <= I));
+    const int wd = (wave * row.per_wave) / 64 + j;
+    if (lane == 0 && wd < words) bits[wd] = m;
+  }
+  __syncthreads();
+  // word w to thread w (and w + NT, ...): counts, a block scan, the indices
+  int pre = 0;
+  for (int w0 = 0; w0 < words; w0 += NT) {
+    const int w = w0 + tid;
+    const unsigned long long m = w < words ? bits[w] : 0ull;
+    const unsigned c = (unsigned)__popcll(m);
+    const unsigned incl = wave_incl_scan(c);
+    if (lane == 63) scan[wave] = (int)incl;
+    __syncthreads();
+    int base = pre + (int)(incl - c);
+    for (int v = 0; v < wave; v++) base += scan[v];
+    int tot = 0;
+    for (int v = 0; v < NW; v++) tot += scan[v];
+    unsigned long long r = m;
+    while (r != 0ull) {
+      const int bit = __builtin_ctzll(r);
+      dst[base++] = w * 64 + bit;
+      r &= r - 1ull;
+    }
+    pre += tot;
+    __syncthreads();  // scan is reused by the next block of words
+  }
 }
 
 // Entries of each wave's list in select_rows: the lists fill sm.hist and
@@ -486,7 +799,7 @@ __device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k,
     }
   } else {
     __syncthreads();  // every list entry is copied out before whist is reused
-    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm);
+    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm, sm.whist);
     const unsigned T = sm.thr_key;
     const int I = sm.thr_idx;
     auto taken = [&](int i, unsigned key) -> bool {
@@ -622,7 +935,7 @@ __device__ __forceinline__ void block_select(Load load_score, int S, int k, int3
     if (i < S) atomicAdd(&sm.hist[lin_bin(key_score(key), lo, scale)], 1u);
   });
   __syncthreads();
-  select_from_histogram<NT, KREG>(row, k, out_idx, out_val, sm, lo, scale);
+  select_from_histogram<NT, KREG>(row, k, out_idx, out_val, sm, lo, scale, sm.whist);
 }
 
 }  // namespace loki

@@ -477,10 +477,122 @@ def test_provisional_range_far_from_later_scores(L, dtype, B, nh, S, k):
     H.log(f"  {res}")
 
 
+# The one-launch kernel with one query head per workgroup and its whole row of
+# scores in LDS (rows up to 32768 tokens, grouped heads of any size): 512
+# threads up to 16384 tokens (two workgroups per compute unit), 1024 above;
+# helpers for single-head rows when the heads leave workgroup slots free (a
+# multiple of 8 heads, k >= 256); grouped heads padded to whole blocks of 8
+# (b, kv) units; binning over mean +- 6 sd above 16384 tokens.
+HEAD_CASES = {
+    "g1-pairs-20k-heavy": dict(dtype="bf16", B=2, Hq=8, Hkv=8, S=20000, k=2500, heavy_frac=0.02),
+    "g1-pairs-512thr": dict(dtype="f16", B=1, Hq=8, Hkv=8, S=9000, k=300),
+    "g1-small-k-no-pairs": dict(dtype="f16", B=1, Hq=8, Hkv=8, S=9000, k=100),
+    "g1-32768-heavy": dict(dtype="bf16", B=1, Hq=8, Hkv=8, S=32768, k=4096, heavy_frac=0.02),
+    "g1-odd-heads": dict(dtype="f16", B=1, Hq=5, Hkv=5, S=12345, k=1234),
+    "g1-k-eq-S": dict(dtype="f16", B=1, Hq=8, Hkv=8, S=4500, k=4500),
+    "g1-k1": dict(dtype="bf16", B=1, Hq=8, Hkv=8, S=5000, k=1),
+    "g4-xcd-padding": dict(dtype="bf16", B=3, Hq=12, Hkv=3, S=6000, k=800),
+    "g4-16k": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=16384, k=2048),
+    "g2-f32": dict(dtype="f32", B=2, Hq=4, Hkv=2, S=7000, k=700, tau=20.0),
+    "g16-f16": dict(dtype="f16", B=1, Hq=16, Hkv=1, S=5000, k=400),
+    "g8-cap-above-seq": dict(dtype="f16", B=1, Hq=16, Hkv=2, S=4700, S_cap=5000, k=500),
+    "g2-16k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=16384, k=2048),
+    "g6": dict(dtype="f16", B=1, Hq=12, Hkv=2, S=7000, k=900),
+    "g3-odd-group": dict(dtype="bf16", B=2, Hq=6, Hkv=2, S=9000, k=1000),
+}
+
+
+@pytest.mark.parametrize("case", list(HEAD_CASES), ids=list(HEAD_CASES))
+def test_decode_head_kernel(L, case):
+    wl = _small(**HEAD_CASES[case])
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    assert L.decode_plan(dev["desc"], wl.d, wl.k), f"{case} is meant to take one launch"
+    H.log(f"decode (one head per workgroup) {case}: {W.describe(wl)}")
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  {res}")
+
+
+HEAD_APPEND = {
+    "g1-pairs-append": dict(dtype="bf16", B=2, Hq=8, Hkv=8, S=20000, S_cap=20100, k=2500,
+                            heavy_frac=0.02),
+    "g1-pairs-append-selected": dict(dtype="f16", B=1, Hq=8, Hkv=8, S=9000, S_cap=9000, k=600,
+                                     selected=True),
+    "g4-append-selected": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=6000, S_cap=6100, k=700,
+                               selected=True),
+    "g4-append-in-first-batch": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=4200, S_cap=4300, k=300,
+                                     selected=True),
+    "g1-32768-append": dict(dtype="bf16", B=1, Hq=8, Hkv=8, S=32768, S_cap=32768, k=4096,
+                            heavy_frac=0.02),
+}
+
+
+@pytest.mark.parametrize("case", list(HEAD_APPEND), ids=list(HEAD_APPEND))
+def test_decode_append_head_kernel(L, case):
+    kw = dict(HEAD_APPEND[case])
+    selected = kw.pop("selected", False)
+    wl = _small(append=True, **kw)
+    assert L.decode_plan(H.make_desc(wl, 32), wl.d, wl.k, True)
+    H.log(f"decode_append (one head per workgroup) {case}: {W.describe(wl)}")
+    _decode_append_check(L, wl, separate=False, selected=selected)
+
+
+def test_head_kernel_ties_radix_passes(L):
+    """Panel coordinates drawn from 12 distinct rows: every score is tied with
+    hundreds of others, the bin of the k-th score cannot be split, and the
+    selection resolves it by radix passes and the lower-index rule."""
+    wl = _small("f16", B=1, Hq=8, Hkv=8, S=9000, k=1000)
+    x = W.generate(wl)
+    K = W.from_storage(x["krot"], "f16")
+    g = np.random.default_rng(23)
+    pick = g.integers(0, 12, size=(wl.B, wl.Hkv, wl.S))
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            K[b, h, :wl.S, :32] = K[b, h, pick[b, h], :32]
+    x["krot"] = W.to_storage(K, "f16")
+    dev = H.upload(wl, x)
+    assert L.decode_plan(dev["desc"], wl.d, wl.k)
+    out, idx = H.run_decode(wl, dev)
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  ties: {res}")
+    # exact ties must follow the lower-index rule exactly: the GPU's fp32
+    # scores of equal rows are equal, so the sets match the oracle's
+    r = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.k, "f16")
+    s = oracle.decode(x["q"], x["krot"], x["v"], x["P"], wl.d, wl.k, "f16")["scores"]
+    for h in range(wl.Hq):
+        srt = np.sort(s[0, h])[::-1]
+        if srt[wl.k - 1] - srt[wl.k] > 1e-3 * abs(srt[wl.k - 1]):
+            assert np.array_equal(idx[0, h], r["idx"][0, h])
+
+
+@pytest.mark.parametrize("dtype,B,nh,S,k", [("bf16", 2, 8, 20000, 2500), ("f16", 1, 8, 9000, 700)])
+def test_head_kernel_helpers_match_solo(L, dtype, B, nh, S, k):
+    """Helpers of the one-head-per-workgroup kernel against the solo heads:
+    the same index sets, outputs equal up to fp32 summation order and
+    bit-identical from launch to launch."""
+    wl = _small(dtype, B=B, Hq=nh, Hkv=nh, S=S, k=k)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    ws = L.empty_workspace(dev["desc"], wl.d, wl.k)
+    out_solo, idx_solo = _decode_with(L, wl, dev, L.FLAG_NO_HELPERS, ws)
+    first = None
+    for rep in range(3):
+        out, idx = _decode_with(L, wl, dev, 0, ws)
+        assert np.array_equal(idx, idx_solo)
+        assert H.rel_err_rows(out, out_solo).max() < 1e-5
+        if first is None:
+            first = out
+        else:
+            assert np.array_equal(out, first), f"launch {rep} differs from launch 0"
+    res = H.full_parity(wl, x, out, idx)
+    H.log(f"  head helpers {dtype}: {res}")
+
+
 def test_launch_plan(L):
     """Which workloads take the one-launch kernel."""
     expect = {"single_head_f32": True, "llama2_7b_f16": True, "llama2_13b_f16": True,
-              "long_context_bf16": False, "gqa_llama3_8b_bf16": False}
+              "long_context_bf16": True, "gqa_llama3_8b_bf16": True}
     for name, one in expect.items():
         wl = W.get(name)
         desc = H.make_desc(wl, 32)
@@ -840,8 +952,10 @@ def test_workload_full_size(L, name):
 OUT16_CASES = {
     "one-launch-g1-helpers": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1500, k=300),
     "one-launch-g4": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, k=200),
-    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100),
-    "separate-f32": dict(dtype="f32", B=2, Hq=4, Hkv=4, S=5000, k=300),
+    "head-kernel-g2": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100),
+    "head-kernel-f32": dict(dtype="f32", B=2, Hq=4, Hkv=4, S=5000, k=300),
+    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100, separate=True),
+    "separate-f32": dict(dtype="f32", B=2, Hq=4, Hkv=4, S=5000, k=300, separate=True),
     "append-one-launch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1200, S_cap=1300, k=200,
                               append=True),
 }
@@ -857,13 +971,15 @@ def _bits(t):
 def test_out_dtype(L, case, odt):
     """A 16-bit output is the fp32 output of the same step rounded once to
     nearest-even (torch's conversion), bit for bit."""
-    wl = _small(**OUT16_CASES[case])
+    kw = dict(OUT16_CASES[case])
+    flags = L.FLAG_SEPARATE_KERNELS if kw.pop("separate", False) else 0
+    wl = _small(**kw)
     H.log(f"out_dtype {odt} {case}: {W.describe(wl)}")
     x = W.generate(wl)
     outs = {}
     for name, dt in (("f32", L.F32), (odt, L.NAME_CODE[odt])):
         dev = H.upload(wl, x)   # fresh caches: the appending step rewrites row S-1
-        desc = dev["desc"].with_out_dtype(dt)
+        desc = dev["desc"].with_out_dtype(dt).with_flags(flags)
         if wl.append:
             outs[name] = L.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"],
                                          dev["v"], dev["P"], wl.d, wl.k, desc)
@@ -927,8 +1043,11 @@ def test_decode_scores_out(L, append):
 
 GRAPH_CASES = {
     "one-launch-g1": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1500, k=300),
+    "head-kernel-pairs": dict(dtype="bf16", B=1, Hq=8, Hkv=8, S=12000, k=1500),
+    "head-kernel-g4-append": dict(dtype="bf16", B=2, Hq=8, Hkv=2, S=6000, S_cap=6100, k=700,
+                                  append=True),
     "one-launch-g4": dict(dtype="bf16", B=2, Hq=16, Hkv=4, S=1800, k=200),
-    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100),
+    "separate-split-k": dict(dtype="bf16", B=2, Hq=4, Hkv=2, S=6000, k=1100, separate=True),
     "append-one-launch": dict(dtype="f16", B=2, Hq=4, Hkv=4, S=1200, S_cap=1300, k=200,
                               append=True),
 }
@@ -942,11 +1061,14 @@ def test_decode_graph_replay(L, case, helpers):
     every replay equals the eager step bit for bit.  A replay reuses the
     captured launch tag of the helper pairs; the second workgroup of a pair
     clears the pair's flag, so every replay pairs afresh."""
-    wl = _small(**GRAPH_CASES[case])
+    kw = dict(GRAPH_CASES[case])
+    flags = (L.FLAG_SEPARATE_KERNELS if kw.pop("separate", False) else 0) | \
+        (0 if helpers else L.FLAG_NO_HELPERS)
+    wl = _small(**kw)
     H.log(f"graph replay {case} helpers={helpers}: {W.describe(wl)}")
     x = W.generate(wl)
     dev = H.upload(wl, x)
-    desc = dev["desc"] if helpers else dev["desc"].with_flags(L.FLAG_NO_HELPERS)
+    desc = dev["desc"].with_flags(flags)
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.B, wl.Hq, wl.k), dtype=torch.int32, device="cuda")
     ws = L.empty_workspace(desc, wl.d, wl.k)
