@@ -41,9 +41,11 @@ def metric_label(name):
     return ("Loki decode-attn µs/step & achieved HBM GB/s (% peak), "
             + SHAPE_LABEL.get(name, name))
 KERNEL_SOURCES = {"score": "score.hip", "attend": "attend.hip", "topk": "topk.hip",
-                  "rotate_query": "project.hip", "fused": "fused.hip"}
+                  "rotate_query": "project.hip", "fused": "fused.hip", "head": "head.hip"}
 KERNEL_NAMES = {"score": "score_panel_kernel", "attend": "attend_kernel", "topk": "topk_kernel",
-                "rotate_query": "project_kernel", "fused": "fused_kernel"}
+                "rotate_query": "project_kernel", "fused": "fused_kernel", "head": "head_kernel"}
+# one-launch plans of loki_decode_plan: the kernel that runs the step
+PLAN_KERNEL = {1: "fused", 2: "head"}
 
 
 def parse():
@@ -147,7 +149,8 @@ def main():
     k_new = up(x["k_new"]) if wl.append else None
     v_new = up(x["v_new"]) if wl.append else None
     stream = torch.cuda.current_stream()
-    one_launch = loki.decode_plan(desc, wl.d, wl.k, wl.append)
+    plan_code = loki.decode_kernel(desc, wl.d, wl.k, wl.append)
+    one_launch = plan_code != 0
     vp = ctypes.c_void_p
 
     def make_calls(d_, st_=stream):
@@ -425,8 +428,8 @@ def main():
     attend_bytes = es * wl.B * wl.Hq * 2 * wl.k * wl.D
     if one_launch:
         # the step is one kernel: K back-to-back launches timed above
-        dom, dom_us, dom_bytes = "fused", ms_per_step * 1e3, alg_bytes
-        kernels = {"fused": round(dom_us, 2)}
+        dom, dom_us, dom_bytes = PLAN_KERNEL[plan_code], ms_per_step * 1e3, alg_bytes
+        kernels = {dom: round(dom_us, 2)}
     else:
         per_kernel_bytes = {"score": score_bytes, "attend": attend_bytes}
         dom = max(["score", "attend"], key=lambda n: per_kernel[n])
@@ -454,7 +457,8 @@ def main():
         "data": "synthetic",
         "config": {**W.describe(wl), "algorithmic_bytes_per_step": alg_bytes,
                    "cache_copies_cycled": args.sets},
-        "launch_plan": "one kernel" if one_launch else "separate kernels",
+        "launch_plan": {0: "separate kernels", 1: "one kernel (one workgroup per (b, kv))",
+                        2: "one kernel (one workgroup per query head)"}[plan_code],
         "spread": spread,
         "graph": graph,
         "kernel_us": kernels,
@@ -597,7 +601,9 @@ def time_workload(name, args, headline=None):
     desc = loki.Desc(batch=wl.B, n_q_heads=wl.Hq, n_kv_heads=wl.Hkv, head_dim=wl.D,
                      seq_len=wl.S, seq_capacity=wl.capacity, panel_dim=wl.d,
                      dtype=loki.NAME_CODE[wl.dtype])
-    plan = "one kernel" if loki.decode_plan(desc, wl.d, wl.k, wl.append) else "separate kernels"
+    code = loki.decode_kernel(desc, wl.d, wl.k, wl.append)
+    plan = {0: "separate kernels", 1: "one kernel (one workgroup per (b, kv))",
+            2: "one kernel (one workgroup per query head)"}[code]
     if headline is not None:
         us, spread, dense_us, par, idx_h = headline
         sets_n = args.sets

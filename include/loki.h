@@ -78,7 +78,8 @@ typedef struct {
   int32_t batch;        /* B >= 1 */
   int32_t n_q_heads;    /* Hq >= 1 */
   int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq/Hkv in 1..16 */
-  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t head_dim;     /* D: 64, 96 or 128 (the poster page's "More on figures"
+                           reports keys of 128 or 96 dimensions) */
   int32_t seq_len;      /* S: tokens attended, 1 <= S <= seq_capacity */
   int32_t seq_capacity; /* S_cap: rows allocated per (b, kv) in both caches */
   int32_t panel_dim;    /* dp: leading rotated coordinates stored as the scoring
@@ -121,12 +122,16 @@ int loki_kcache_elems(const loki_desc* desc, size_t* n_elems);
 int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes);
 
 /*
- * Launch plan of a decode step: *one_launch = 1 when loki_decode (append = 0)
- * or loki_decode_append (append = 1) with these arguments runs as a single
- * kernel (rotation, scores in LDS, top-k, attention per (b, kv) workgroup:
- * needs d == panel_dim, head_dim 128, Hq/Hkv in {1, 2, 4}, S <= 4096 and the
- * group's scores within the LDS budget; the same conditions with or without
- * append), 0 when it runs as separate launches.
+ * Launch plan of a decode step: *one_launch is nonzero when loki_decode
+ * (append = 0) or loki_decode_append (append = 1) with these arguments runs as
+ * a single kernel, 0 when it runs as separate launches (d != panel_dim, head
+ * dimension 64, or LOKI_FLAG_SEPARATE_KERNELS).  1: one workgroup per
+ * (b, kv) with its group's scores in LDS (head_dim 128, Hq/Hkv in {1, 2, 4},
+ * S <= 4096, the group's scores and index lists within the LDS budget).
+ * 2: otherwise, up to S = 32768: one workgroup per query head with its whole
+ * row of scores in LDS (plus helper workgroups sharing the heads' attention
+ * when the heads leave compute units free).  The plan is the same with or
+ * without append.
  */
 int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_launch);
 

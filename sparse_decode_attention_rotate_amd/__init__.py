@@ -178,12 +178,18 @@ def workspace_bytes(desc: Desc, d: int, k: int) -> int:
     return n.value
 
 
-def decode_plan(desc: Desc, d: int, k: int, append: bool = False) -> bool:
-    """True when the decode step runs as one kernel launch."""
+def decode_kernel(desc: Desc, d: int, k: int, append: bool = False) -> int:
+    """Launch plan code of loki_decode_plan: 0 separate launches, 1 one
+    workgroup per (b, kv) unit, 2 one workgroup per query head."""
     one = ctypes.c_int()
     _check(_lib.loki_decode_plan(ctypes.byref(desc.c()), d, k, int(append), ctypes.byref(one)),
            "loki_decode_plan")
-    return bool(one.value)
+    return one.value
+
+
+def decode_plan(desc: Desc, d: int, k: int, append: bool = False) -> bool:
+    """True when the decode step runs as one kernel launch."""
+    return decode_kernel(desc, d, k, append) != 0
 
 
 def empty_kcache(desc: Desc, device="cuda") -> torch.Tensor:

@@ -87,11 +87,15 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendParams p) {
 // are loaded together, and each later batch of kBatch splits is one round
 // trip instead of one per split.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
+__global__ __launch_bounds__(kLaneDim<D>) void combine_kernel(AttendParams p) {
+  // NTH threads (D, or 128 for D = 96): thread t loads the (m, l) of splits
+  // t, t + NTH, ... and, when t < D, forms output coordinate t
+  constexpr int NTH = kLaneDim<D>;
   constexpr int kBatch = 8;
-  constexpr int kWaves = D / 64;
-  __shared__ float sw[D], sl[D], smax[kWaves];
+  constexpr int kWaves = NTH / 64;
+  __shared__ float sw[NTH], sl[NTH], smax[kWaves];
   const int tid = threadIdx.x, ns = p.nsplit;
+  const int col = tid < D ? tid : 0;  // threads past D read column 0 and store nothing
   const size_t bh = blockIdx.x;
   const size_t stride = D + 2;
   const float* part = p.part + bh * ns * stride;
@@ -103,9 +107,9 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
   }
   float v[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; j++) v[j] = j < ns ? part[j * stride + 2 + tid] : 0.f;
+  for (int j = 0; j < kBatch; j++) v[j] = j < ns ? part[j * stride + 2 + col] : 0.f;
   float m = mo;
-  for (int s = tid + D; s < ns; s += D) m = fmaxf(m, part[s * stride]);
+  for (int s = tid + NTH; s < ns; s += NTH) m = fmaxf(m, part[s * stride]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) smax[tid >> 6] = m;
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
   for (int w = 1; w < kWaves; w++) M = fmaxf(M, smax[w]);
 
   float L = 0.f, a = 0.f;
-  for (int b0 = 0; b0 < ns; b0 += D) {
+  for (int b0 = 0; b0 < ns; b0 += NTH) {
     if (b0 > 0) {
       __syncthreads();  // every thread is done with the previous block's weights
       mo = -INFINITY;
@@ -128,12 +132,12 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
     sw[tid] = mo == -INFINITY ? 0.f : exp2f(mo - M);
     sl[tid] = lo;
     __syncthreads();
-    const int nb = min(D, ns - b0);
+    const int nb = min(NTH, ns - b0);
     for (int j0 = 0; j0 < nb; j0 += kBatch) {
       if (b0 + j0 > 0) {  // the first batch was loaded up front
 #pragma unroll
         for (int j = 0; j < kBatch; j++)
-          v[j] = j0 + j < nb ? part[(b0 + j0 + j) * stride + 2 + tid] : 0.f;
+          v[j] = j0 + j < nb ? part[(b0 + j0 + j) * stride + 2 + col] : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < kBatch; j++) {
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(D) void combine_kernel(AttendParams p) {
       }
     }
   }
-  store_out(p.out, bh * D + tid, a / L, p.sh.odt);
+  if (tid < D) store_out(p.out, bh * D + tid, a / L, p.sh.odt);
 }
 
 template <int DT, int D>
@@ -181,13 +185,17 @@ hipError_t launch_d(const AttendParams& p, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  combine_kernel<D><<<dim3((unsigned)(p.sh.B * p.sh.Hq)), D, 0, st>>>(p);
+  combine_kernel<D><<<dim3((unsigned)(p.sh.B * p.sh.Hq)), kLaneDim<D>, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const AttendParams& p, hipStream_t st) {
-  return p.sh.D == 128 ? launch_d<DT, 128>(p, st) : launch_d<DT, 64>(p, st);
+  switch (p.sh.D) {
+    case 128: return launch_d<DT, 128>(p, st);
+    case 96: return launch_d<DT, 96>(p, st);
+    default: return launch_d<DT, 64>(p, st);
+  }
 }
 
 }  // namespace

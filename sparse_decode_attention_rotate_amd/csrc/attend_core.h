@@ -28,11 +28,18 @@ namespace loki {
 
 constexpr int kRowsPerBatch = 4;  // default rows per lane group per load batch
 
+// Lane geometry of a row of D elements: a power-of-two number of 16-byte
+// lanes.  D = 96 takes the lanes of 128 elements; the lanes past D read
+// nothing and contribute zeros.
+template <int D>
+constexpr int kLaneDim = D == 96 ? 128 : D;
+
 template <int DT, int D, int NT>
 struct AttendGeom {
   static constexpr int EB = Elem<DT>::kBytes;
   static constexpr int E = Elem<DT>::kPerVec;
-  static constexpr int LPR = D * EB / 16;         // lanes per row
+  static constexpr int DL = kLaneDim<D>;          // row elements covered by the lanes
+  static constexpr int LPR = DL * EB / 16;        // lanes per row
   static constexpr int RPI = 64 / LPR;            // rows per wave instruction
   static constexpr int NG = (NT / 64) * RPI;      // lane groups per workgroup
 };
@@ -40,7 +47,7 @@ struct AttendGeom {
 template <int DT, int D, int NT>
 struct AttendSmem {
   float red_m[AttendGeom<DT, D, NT>::NG], red_l[AttendGeom<DT, D, NT>::NG];
-  float accs[AttendGeom<DT, D, NT>::NG][D];
+  float accs[AttendGeom<DT, D, NT>::NG][AttendGeom<DT, D, NT>::DL];
 };
 
 // All NT threads call this together.  qrow: the query in the rotated basis
@@ -70,16 +77,18 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
   const int j0 = c * E;
 
   // qr slice, pre-multiplied by scale*log2(e); in the split variant the
-  // coordinates below dp are already in the low-dim partial logit.
+  // coordinates below dp are already in the low-dim partial logit.  Lanes
+  // past the row (D = 96) hold zeros and read nothing.
+  const bool in_row = j0 < D;
   float qv[E];
 #pragma unroll
   for (int e = 0; e < E; e++) {
     const int j = j0 + e;
-    const float v = qrow[j] * scale_log2;
+    const float v = in_row ? qrow[j] * scale_log2 : 0.f;
     qv[e] = ((SPLIT && j < sh.dp) || (LOW && j >= kdim)) ? 0.f : v;
   }
   // byte offset of this lane's key chunk inside a row's part of the cache
-  const bool k_needed = (!SPLIT || j0 >= sh.dp) && (!LOW || j0 < kdim);
+  const bool k_needed = in_row && (!SPLIT || j0 >= sh.dp) && (!LOW || j0 < kdim);
   const bool in_panel = j0 < sh.dp;
   const uint32_t k_row_bytes = (uint32_t)((in_panel ? sh.dp : sh.kl.rest) * EB);
   const uint32_t k_base = (uint32_t)((in_panel ? (size_t)j0 : sh.kl.rest_off + (j0 - sh.dp)) * EB);
@@ -98,7 +107,7 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
       const int r = rbase + q * NG;
       const int t = r < nr ? sidx[r] : -1;
       const uint32_t ko = (t >= 0 && k_needed) ? k_base + (uint32_t)t * k_row_bytes : kOutOfRange;
-      const uint32_t vo = t >= 0 ? ((uint32_t)t * D + j0) * EB : kOutOfRange;
+      const uint32_t vo = (t >= 0 && in_row) ? ((uint32_t)t * D + j0) * EB : kOutOfRange;
       kb[q] = STREAM ? load16_stream(krs, ko) : load16(krs, ko);
       vb[q] = STREAM ? load16_stream(vrs, vo) : load16(vrs, vo);
     }

@@ -282,7 +282,11 @@ hipError_t launch_d(const CalibParams& p, hipStream_t st) {
 
 template <int DT>
 hipError_t launch_dt(const CalibParams& p, hipStream_t st) {
-  return p.sh.D == 128 ? launch_d<DT, 128>(p, st) : launch_d<DT, 64>(p, st);
+  switch (p.sh.D) {
+    case 128: return launch_d<DT, 128>(p, st);
+    case 96: return launch_d<DT, 96>(p, st);
+    default: return launch_d<DT, 64>(p, st);
+  }
 }
 
 }  // namespace

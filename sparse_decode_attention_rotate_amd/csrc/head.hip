@@ -80,10 +80,10 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   constexpr int DP = LPT * 16 / Elem<DT>::kBytes;  // panel width (== d)
   constexpr int TPP = NT / LPT;                    // tokens per pass over the panel
   constexpr int NB = kHeadBatch;
-  // rotation: 32 column quads x NT/32 row slots
+  // rotation: 32 column quads x NT/32 row slots (D/4 <= 32 quads in use)
   constexpr int RSR = NT / 32, NR = (D + RSR - 1) / RSR;
   constexpr int NXV = (GR * D + NT - 1) / NT;
-  static_assert(D == 128, "32 column quads");
+  static_assert(D % 4 == 0 && D <= 128, "at most 32 column quads");
   using L = HeadLds<DT, D, NT, GR>;
 
   extern __shared__ __align__(16) unsigned char reuse[];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
 #pragma unroll
   for (int u = 0; u < NR; u++) {
     const int row = rs + RSR * u;
-    pl[u] = load16(Prs, row < D ? (row * D + 4 * cq) * 4 : kOutOfRange);
+    pl[u] = load16(Prs, (row < D && 4 * cq < D) ? (row * D + 4 * cq) * 4 : kOutOfRange);
   }
   float xv[NXV];
 #pragma unroll
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
     for (int r = 0; r < GR; r++)
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) a[r][cc] += __shfl_xor(a[r][cc], 32, 64);
-    if (lane < 32)
+    if (lane < 32 && 4 * cq < D)
 #pragma unroll
       for (int r = 0; r < GR; r++)
 #pragma unroll
@@ -423,38 +423,43 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
 // compute unit) while a row's scores fit half of the LDS, else 1024.
 int head_threads(int S) { return S <= 512 * 32 && S * 4 <= 64 * 1024 ? 512 : 1024; }
 
-template <int DT, int LPT, int NT, bool APPEND>
+template <int DT, int D, int LPT, int NT, bool APPEND>
 hipError_t launch_v(const HeadParams& p, hipStream_t st) {
-  const size_t dyn = HeadLds<DT, 128, NT, APPEND ? 2 : 1>::bytes(p.sh.S, p.k);
+  const size_t dyn = HeadLds<DT, D, NT, APPEND ? 2 : 1>::bytes(p.sh.S, p.k);
   const dim3 grid((unsigned)(p.n_slots + p.n_help));
-  head_kernel<DT, 128, LPT, NT, 32, APPEND><<<grid, NT, dyn, st>>>(p);
+  head_kernel<DT, D, LPT, NT, 32, APPEND><<<grid, NT, dyn, st>>>(p);
   return hipGetLastError();
 }
 
-template <int DT, int LPT, bool APPEND>
+template <int DT, int D, int LPT, bool APPEND>
 hipError_t launch_a(const HeadParams& p, hipStream_t st) {
-  return head_threads(p.sh.S) == 512 ? launch_v<DT, LPT, 512, APPEND>(p, st)
-                                     : launch_v<DT, LPT, 1024, APPEND>(p, st);
+  return head_threads(p.sh.S) == 512 ? launch_v<DT, D, LPT, 512, APPEND>(p, st)
+                                     : launch_v<DT, D, LPT, 1024, APPEND>(p, st);
 }
 
-template <int DT, int LPT>
+template <int DT, int D, int LPT>
 hipError_t launch_lpt(const HeadParams& p, hipStream_t st) {
-  return p.k_new ? launch_a<DT, LPT, true>(p, st) : launch_a<DT, LPT, false>(p, st);
+  return p.k_new ? launch_a<DT, D, LPT, true>(p, st) : launch_a<DT, D, LPT, false>(p, st);
+}
+
+template <int DT, int D>
+hipError_t launch_d(const HeadParams& p, hipStream_t st) {
+  const int lpt = p.sh.dp * Elem<DT>::kBytes / 16;
+  return lpt == 4 ? launch_lpt<DT, D, 4>(p, st) : launch_lpt<DT, D, 8>(p, st);
 }
 
 template <int DT>
 hipError_t launch_dt(const HeadParams& p, hipStream_t st) {
-  const int lpt = p.sh.dp * Elem<DT>::kBytes / 16;
-  return lpt == 4 ? launch_lpt<DT, 4>(p, st) : launch_lpt<DT, 8>(p, st);
+  return p.sh.D == 96 ? launch_d<DT, 96>(p, st) : launch_d<DT, 128>(p, st);
 }
 
 // Static LDS of a built variant (the compiler's figure), read once.
-template <int DT, int LPT, int NT, bool APPEND>
+template <int DT, int D, int LPT, int NT, bool APPEND>
 size_t static_lds() {
   static const size_t bytes = [] {
     hipFuncAttributes a{};
     if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(
-                                     &head_kernel<DT, 128, LPT, NT, 32, APPEND>)) != hipSuccess)
+                                     &head_kernel<DT, D, LPT, NT, 32, APPEND>)) != hipSuccess)
       return (size_t)1 << 30;  // unknown: the variant is not used
     return (size_t)a.sharedSizeBytes;
   }();
@@ -463,17 +468,18 @@ size_t static_lds() {
 
 // LDS of the appending variant (the larger one) that a shape would take:
 // dynamic + static bytes.
-template <int DT, int LPT>
+template <int DT, int D, int LPT>
 size_t lds_for(const Shape& sh, int k) {
   if (head_threads(sh.S) == 512)
-    return HeadLds<DT, 128, 512, 2>::bytes(sh.S, k) + static_lds<DT, LPT, 512, true>();
-  return HeadLds<DT, 128, 1024, 2>::bytes(sh.S, k) + static_lds<DT, LPT, 1024, true>();
+    return HeadLds<DT, D, 512, 2>::bytes(sh.S, k) + static_lds<DT, D, LPT, 512, true>();
+  return HeadLds<DT, D, 1024, 2>::bytes(sh.S, k) + static_lds<DT, D, LPT, 1024, true>();
 }
 
 template <int DT>
 size_t lds_dt(const Shape& sh, int k) {
   const int lpt = sh.dp * Elem<DT>::kBytes / 16;
-  return lpt == 4 ? lds_for<DT, 4>(sh, k) : lds_for<DT, 8>(sh, k);
+  if (sh.D == 96) return lpt == 4 ? lds_for<DT, 96, 4>(sh, k) : lds_for<DT, 96, 8>(sh, k);
+  return lpt == 4 ? lds_for<DT, 128, 4>(sh, k) : lds_for<DT, 128, 8>(sh, k);
 }
 
 }  // namespace
@@ -483,7 +489,8 @@ int head_kernel_threads(const Shape& sh) { return head_threads(sh.S); }
 bool head_supported(const Shape& sh, int d, int k) {
   const int eb = sh.dtype == F32 ? 4 : 2;
   const int lpt = sh.dp * eb / 16;
-  if (!(d == sh.dp && sh.D == 128 && (lpt == 4 || lpt == 8) && sh.S <= 1024 * 32 && k >= 1))
+  if (!(d == sh.dp && (sh.D == 128 || sh.D == 96) && (lpt == 4 || lpt == 8) &&
+        sh.S <= 1024 * 32 && k >= 1))
     return false;
   // the appending variant (the larger) must fit the compute unit's LDS
   size_t lds = 0;

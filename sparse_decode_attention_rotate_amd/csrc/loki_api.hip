@@ -65,8 +65,8 @@ int check_desc(const loki_desc* d, Shape* sh) {
     return fail(LOKI_EINVAL, "dtype %d is not a loki_dtype", d->dtype);
   if (d->out_dtype != LOKI_F32 && d->out_dtype != LOKI_F16 && d->out_dtype != LOKI_BF16)
     return fail(LOKI_EINVAL, "out_dtype %d is not a loki_dtype", d->out_dtype);
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(LOKI_EUNSUPPORTED, "head_dim %d (built: 64, 128)", d->head_dim);
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
+    return fail(LOKI_EUNSUPPORTED, "head_dim %d (built: 64, 96, 128)", d->head_dim);
   if (d->seq_len < 1 || d->seq_capacity < d->seq_len || d->seq_capacity > (1 << 30))
     return fail(LOKI_EINVAL, "need 1 <= seq_len (%d) <= seq_capacity (%d) <= 2^30",
                 d->seq_len, d->seq_capacity);
@@ -439,8 +439,9 @@ int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_l
   if (d < 1 || d > sh.D) return fail(LOKI_EINVAL, "d = %d outside [1, %d]", d, sh.D);
   if (k < 1 || k > sh.S) return fail(LOKI_EINVAL, "k = %d outside [1, %d]", k, sh.S);
   (void)append;  // the one-launch kernel appends too
-  *one_launch = (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) &&
-                 (fused_supported(sh, d, k) || head_supported(sh, d, k))) ? 1 : 0;
+  *one_launch = 0;
+  if (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS))
+    *one_launch = fused_supported(sh, d, k) ? 1 : (head_supported(sh, d, k) ? 2 : 0);
   return LOKI_OK;
 }
 

@@ -211,7 +211,9 @@ __global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams
   const Shape& sh = p.sh;
   const size_t head = blockIdx.y;
   const int kv = (int)(head % sh.Hkv);
+  // (D = 96: the threads past NSLOT*D only help stage the keys)
   const int j = threadIdx.x % D, slot = threadIdx.x / D;
+  const bool has_col = slot < NSLOT;
   float pc[D];
   {
     const float* P = p.P + (size_t)kv * D * D;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_valu_kernel(PrefillParams
     }
     __syncthreads();
 #pragma unroll 1
-    for (int r = slot; r < RUN && t0 + r < t_end; r += NSLOT) {
+    for (int r = slot; has_col && r < RUN && t0 + r < t_end; r += NSLOT) {
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < D; i += 4) {
@@ -308,7 +310,11 @@ hipError_t launch_dt(const PrefillParams& p, hipStream_t st) {
   if constexpr (DT != F32) {
     if (p.sh.D == 128) return launch_mfma_sized<DT>(p, st);
   }
-  return p.sh.D == 128 ? launch_valu<DT, 128>(p, st) : launch_valu<DT, 64>(p, st);
+  switch (p.sh.D) {
+    case 128: return launch_valu<DT, 128>(p, st);
+    case 96: return launch_valu<DT, 96>(p, st);
+    default: return launch_valu<DT, 64>(p, st);
+  }
 }
 
 }  // namespace

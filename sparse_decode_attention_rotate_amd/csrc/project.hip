@@ -61,7 +61,10 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectParams p) 
   __syncthreads();
 
   // thread (j, rg) forms coordinate j of rows rg, rg + RG, ...: branch-free
+  // (D = 96: the threads past RG*D have no coordinate)
+  static_assert(D * D % (4 * kProjThreads) == 0, "P in whole 16-byte pieces per thread");
   const int j = threadIdx.x % D, rg = threadIdx.x / D;
+  if (rg >= RG) return;  // no barrier follows
   float acc[ACC];
 #pragma unroll
   for (int a = 0; a < ACC; a++) acc[a] = 0.f;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectParams p) 
   }
 
   if (p.k_new) {
-    for (int e = threadIdx.x; e < nb * D; e += kProjThreads) {
+    for (int e = threadIdx.x; e < nb * D; e += RG * D) {
       const int b = b0 + e / D, i = e % D;
       const size_t head = (size_t)b * sh.Hkv + kv;
       copy_elem<DT>(p.vcache, (head * sh.S_cap + (size_t)p.pos) * D + i, p.v_new, head * D + i);
@@ -122,7 +125,11 @@ hipError_t launch_d(const ProjectParams& p, dim3 grid, int rows) {
 
 template <int DT>
 hipError_t launch_dt(const ProjectParams& p, dim3 grid, int rows) {
-  return p.sh.D == 128 ? launch_d<DT, 128>(p, grid, rows) : launch_d<DT, 64>(p, grid, rows);
+  switch (p.sh.D) {
+    case 128: return launch_d<DT, 128>(p, grid, rows);
+    case 96: return launch_d<DT, 96>(p, grid, rows);
+    default: return launch_d<DT, 64>(p, grid, rows);
+  }
 }
 
 }  // namespace

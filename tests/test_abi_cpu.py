@@ -64,7 +64,7 @@ def _desc(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -1), (dict(n_q_heads=3), -1), (dict(n_kv_heads=0), -1),
-    (dict(head_dim=96), -2), (dict(head_dim=256), -2), (dict(dtype=7), -1),
+    (dict(head_dim=80), -2), (dict(head_dim=256), -2), (dict(dtype=7), -1),
     (dict(seq_len=0), -1), (dict(seq_capacity=50), -1), (dict(panel_dim=24), -1),
     (dict(panel_dim=4), -1), (dict(panel_dim=256), -1),
     (dict(n_q_heads=34, n_kv_heads=2), -2), (dict(out_dtype=3), -1), (dict(out_dtype=-1), -1),
@@ -176,3 +176,14 @@ def test_binding_has_no_cpu_path(L):
     q = torch.zeros((2, 4, 128), dtype=torch.float16)
     with pytest.raises(ValueError, match="device memory"):
         L.decode(q, q, q, q, 32, 10, d, workspace=torch.zeros(1), out=torch.zeros((2, 4, 128)))
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_head_dims_built(L, D):
+    """head_dim 64, 96 and 128 are in the domain: sizing calls succeed."""
+    n = ctypes.c_size_t()
+    rc = L.lib.loki_workspace_bytes(ctypes.byref(_desc(L, head_dim=D).c()), 32, 10, ctypes.byref(n))
+    assert rc == 0 and n.value > 0
+    e = ctypes.c_size_t()
+    assert L.lib.loki_kcache_elems(ctypes.byref(_desc(L, head_dim=D).c()), ctypes.byref(e)) == 0
+    assert e.value == 2 * 2 * 128 * D

@@ -34,7 +34,8 @@ def _small(dtype="f16", **kw):
 # ------------------------------------------------------------------ layout
 
 @pytest.mark.parametrize("dtype,dp,D", [("f16", 32, 128), ("bf16", 16, 128), ("f32", 32, 128),
-                                        ("f16", 128, 128), ("f32", 8, 64), ("bf16", 64, 64)])
+                                        ("f16", 128, 128), ("f32", 8, 64), ("bf16", 64, 64),
+                                        ("bf16", 32, 96), ("f32", 64, 96)])
 def test_pack_unpack_layout(L, dtype, dp, D):
     wl = _small(dtype, D=D, S=77, S_cap=100)
     H.log(f"pack/unpack {dtype} dp={dp} D={D}")
@@ -58,9 +59,10 @@ def test_pack_unpack_layout(L, dtype, dp, D):
 
 # --------------------------------------------------------------- rotation
 
-@pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 4), ("f16", 8, 2), ("bf16", 6, 3)])
-def test_rotate_query(L, dtype, Hq, Hkv):
-    wl = _small(dtype, Hq=Hq, Hkv=Hkv, B=5, S=64, k=8)
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f32", 4, 4, 128), ("f16", 8, 2, 128),
+                                            ("bf16", 6, 3, 128), ("f16", 6, 3, 96)])
+def test_rotate_query(L, dtype, Hq, Hkv, D):
+    wl = _small(dtype, Hq=Hq, Hkv=Hkv, B=5, S=64, k=8, D=D)
     H.log(f"rotate {dtype} Hq={Hq} Hkv={Hkv}")
     x = W.generate(wl)
     dev = H.upload(wl, x)
@@ -70,7 +72,7 @@ def test_rotate_query(L, dtype, Hq, Hkv):
     P = x["P"].astype(np.float64)
     g = Hq // Hkv
     bound = np.stack([np.abs(q64[:, h]) @ np.abs(P[h // g]) for h in range(Hq)], axis=1)
-    assert np.all(np.abs(qr - ref) <= 2 * 128 * 2.0 ** -24 * bound + 1e-30)
+    assert np.all(np.abs(qr - ref) <= 2 * D * 2.0 ** -24 * bound + 1e-30)
 
 
 # ----------------------------------------------------------------- append
@@ -83,10 +85,10 @@ def _ulp(r: np.ndarray, dtype: str) -> np.ndarray:
     return 2.0 ** (e - mant)
 
 
-@pytest.mark.parametrize("dtype,dp", [("f32", 32), ("f16", 32), ("bf16", 32), ("f16", 128),
-                                      ("bf16", 16)])
-def test_append_row(L, dtype, dp):
-    wl = _small(dtype, S=50, S_cap=64, k=5, append=True, B=3, Hq=4, Hkv=4)
+@pytest.mark.parametrize("dtype,dp,D", [("f32", 32, 128), ("f16", 32, 128), ("bf16", 32, 128),
+                                        ("f16", 128, 128), ("bf16", 16, 128), ("bf16", 32, 96)])
+def test_append_row(L, dtype, dp, D):
+    wl = _small(dtype, S=50, S_cap=64, k=5, append=True, B=3, Hq=4, Hkv=4, D=D)
     H.log(f"append {dtype} dp={dp}")
     x = W.generate(wl)
     dev = H.upload(wl, x, dp)
@@ -149,7 +151,8 @@ def _random_bits(g, shape, dtype):
 @pytest.mark.parametrize("dtype,D,dp,n,pos", [
     ("f16", 128, 32, 1100, 37), ("bf16", 128, 16, 1100, 0), ("f32", 128, 32, 700, 5),
     ("f16", 128, 128, 64, 0), ("bf16", 128, 64, 1, 1199), ("bf16", 128, 32, 600, 600),
-    ("f16", 64, 16, 300, 3), ("f32", 64, 8, 513, 0)])
+    ("f16", 64, 16, 300, 3), ("f32", 64, 8, 513, 0), ("bf16", 96, 32, 500, 7),
+    ("f32", 96, 32, 130, 1)])
 def test_prefill(L, dtype, D, dp, n, pos):
     S_cap = 1200
     wl = _small(dtype, D=D, S=n, S_cap=S_cap, Hq=3, Hkv=3, d=min(32, D), k=1)
@@ -343,7 +346,8 @@ def test_topk_selected_scores_out(L):
 
 @pytest.mark.parametrize("dtype,D,k,g", [("f16", 128, 300, 1), ("bf16", 128, 128, 2),
                                          ("f32", 128, 1, 1), ("f32", 64, 257, 1),
-                                         ("f16", 64, 640, 4), ("bf16", 128, 1000, 1)])
+                                         ("f16", 64, 640, 4), ("bf16", 128, 1000, 1),
+                                         ("bf16", 96, 500, 2), ("f32", 96, 700, 1)])
 def test_attend_given_index_sets(L, dtype, D, k, g):
     wl = _small(dtype, D=D, Hq=2 * g, Hkv=2, S=1500, k=k)
     H.log(f"attend {dtype} D={D} k={k} g={g}")
@@ -422,6 +426,11 @@ E2E = {
     "seq-one": dict(dtype="f16", S=1, k=1, d=8),
     "cap-above-seq": dict(dtype="f16", S=1900, S_cap=2600, k=200),
     "d64-head": dict(dtype="f16", D=64, d=16, tau=20.0),
+    # head dimension 96 (keys of 96 coordinates, the other lanes of a row idle)
+    "d96-f16": dict(dtype="f16", D=96),
+    "d96-bf16-gqa4": dict(dtype="bf16", D=96, Hq=8, Hkv=2, S=5000, k=700),
+    "d96-f32": dict(dtype="f32", D=96, S=2100, k=210, tau=20.0),
+    "d96-long": dict(dtype="bf16", D=96, B=1, Hq=8, Hkv=8, S=20000, k=2500, heavy_frac=0.02),
     "long-11k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=11000, k=1375),
     "long-30k": dict(dtype="bf16", B=1, Hq=2, Hkv=2, S=30000, k=3000, heavy_frac=0.02),
     "long-40k": dict(dtype="f16", B=1, Hq=1, Hkv=1, S=40000, k=5000),
@@ -636,6 +645,14 @@ def test_decode_append_end_to_end(L, dtype, separate):
     _decode_append_check(L, wl, separate)
 
 
+@pytest.mark.parametrize("separate", [False, True], ids=["default", "separate"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_append_head_dim_96(L, dtype, separate):
+    wl = _small(dtype, D=96, S=3100, S_cap=3200, k=300, append=True)
+    H.log(f"decode_append D=96 {dtype} separate={separate}")
+    _decode_append_check(L, wl, separate, selected=True)
+
+
 def test_decode_append_grouped_heads(L):
     """An appending step of grouped heads on the separate path (g = 4, S above
     the one-launch limit), with a new key certain to be selected."""
@@ -796,12 +813,13 @@ def test_concurrent_streams_distinct_workspaces(L, separate):
 
 # ------------------------------------------------ dense decode attention
 
-@pytest.mark.parametrize("dtype,Hq,Hkv,S", [("f16", 4, 4, 3000), ("bf16", 8, 2, 1111),
-                                           ("f32", 2, 2, 700), ("f16", 4, 4, 1)])
-def test_full_attention(L, dtype, Hq, Hkv, S):
+@pytest.mark.parametrize("dtype,Hq,Hkv,S,D", [("f16", 4, 4, 3000, 128), ("bf16", 8, 2, 1111, 128),
+                                             ("f32", 2, 2, 700, 128), ("f16", 4, 4, 1, 128),
+                                             ("bf16", 4, 2, 2500, 96)])
+def test_full_attention(L, dtype, Hq, Hkv, S, D):
     """Dense attention over every cached token: the oracle's decode with
     d = D, k = S (pinned to textbook softmax(q K^T / sqrt(D)) V)."""
-    wl = _small(dtype, Hq=Hq, Hkv=Hkv, S=S, k=min(S, 300), d=min(S, 32))
+    wl = _small(dtype, Hq=Hq, Hkv=Hkv, S=S, k=min(S, 300), d=min(S, 32), D=D)
     H.log(f"full attention {dtype} Hq={Hq} Hkv={Hkv} S={S}")
     x = W.generate(wl)
     dev = H.upload(wl, x)
@@ -835,7 +853,8 @@ def test_full_attention_many_splits(L, dtype, B, Hq, Hkv, S):
 @pytest.mark.parametrize("dtype,Hq,Hkv,S,d,dp,D", [
     ("f16", 4, 4, 3000, 32, 32, 128), ("bf16", 8, 2, 2600, 20, 32, 128),
     ("f32", 2, 2, 1500, 48, 32, 128), ("f16", 4, 2, 700, 128, 32, 128),
-    ("bf16", 2, 2, 513, 7, 16, 128), ("f16", 4, 4, 1100, 16, 16, 64)])
+    ("bf16", 2, 2, 513, 7, 16, 128), ("f16", 4, 4, 1100, 16, 16, 64),
+    ("f16", 4, 2, 1700, 32, 32, 96)])
 def test_pca_attention(L, dtype, Hq, Hkv, S, d, dp, D):
     """PCAAttn: softmax over all tokens of the scaled low-dimensional scores."""
     wl = _small(dtype, Hq=Hq, Hkv=Hkv, S=S, D=D, k=min(S, 300), d=min(d, 32))
@@ -873,7 +892,7 @@ def test_pca_attention_full_size(L):
 
 @pytest.mark.parametrize("dtype,Hkv,n,D,offset", [
     ("f16", 40, 8192, 128, 0.0), ("bf16", 3, 5000, 128, 3.0), ("f32", 2, 3000, 64, 1.0),
-    ("f16", 2, 100, 128, 0.5)])
+    ("f16", 2, 100, 128, 0.5), ("bf16", 3, 4000, 96, 1.0)])
 def test_calibrate(L, dtype, Hkv, n, D, offset):
     """PCA of calibration keys on the GPU against the oracle's fp64 PCA."""
     wl = _small(dtype, Hq=Hkv, Hkv=Hkv, D=D, S=64, k=8)
