@@ -44,7 +44,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libloki_oracle.so")
+# LOKI_ORACLE_LIB names another build of the same source (the sanitizer tier
+# of the tests runs the pins against an AddressSanitizer / UBSan build)
+LIB_PATH = os.environ.get("LOKI_ORACLE_LIB") or os.path.join(HERE, "libloki_oracle.so")
 
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
 NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64}
