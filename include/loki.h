@@ -11,8 +11,9 @@
  *   [A]  briefgpt.xyz keyword page "loki" -- the paper's abstract: tokens are
  *        ranked and selected by attention scores computed in low-dimensional
  *        space;
- *   [T]  deep-diver.github.io NeurIPS-2024 poster page, "TL;DR": full-
- *        dimensional scores only for the selected tokens;
+ *   [T]  deep-diver.github.io NeurIPS-2024 poster page, "TL;DR": exact
+ *        attention scores are computed just for the tokens that the
+ *        low-dimensional ranking keeps;
  *   [F1] same page, "Visual Insights", Figure 1 (right): offline PCA of the
  *        keys, approximate scores in the low-dimensional space, top-k, final
  *        scores with the full-dimensional keys;
@@ -29,7 +30,8 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, at least
- *     16-byte aligned; the library never allocates, frees or synchronises.
+ *     16-byte aligned; the library never allocates or frees device memory
+ *     and never synchronises.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; the call returns after enqueueing.
  *   - Arguments are validated before anything is enqueued: on any error
@@ -38,6 +40,13 @@
  *     (thread-local).  A launch failure reported by the HIP runtime returns
  *     LOKI_EHIP.
  *   - Calls that share a workspace must not overlap in time.
+ *   - Host-side state: per device, the compute-unit count and the address of
+ *     the no-alloc scratch array are cached on first use; per workspace
+ *     pointer that a decode call used with paired workgroups, one 64-bit
+ *     launch counter (16 bytes of host memory each, kept until the process
+ *     ends, so a caller that cycles through many distinct workspaces grows
+ *     that table by one entry per workspace).  No device memory is ever
+ *     allocated.
  *
  * Layouts (element = the storage dtype of loki_desc.dtype)
  *   q        [B, Hq, D]
@@ -79,7 +88,8 @@ typedef struct {
   int32_t n_q_heads;    /* Hq >= 1 */
   int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq/Hkv in 1..16 */
   int32_t head_dim;     /* D: 64, 96 or 128 (the poster page's "More on figures"
-                           reports keys of 128 or 96 dimensions) */
+                           studies models whose key heads have 96 as well as
+                           128 dimensions) */
   int32_t seq_len;      /* S: tokens attended, 1 <= S <= seq_capacity */
   int32_t seq_capacity; /* S_cap: rows allocated per (b, kv) in both caches */
   int32_t panel_dim;    /* dp: leading rotated coordinates stored as the scoring

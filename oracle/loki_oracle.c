@@ -15,8 +15,8 @@
  *     scores are computed in the low-dimensional space, the top-k tokens are
  *     kept, and the final attention scores of those tokens use the
  *     full-dimensional keys.
- *   - same page, "TL;DR": full-dimensional scores are computed only for the
- *     selected tokens.
+ *   - same page, "TL;DR": the exact attention scores are computed just for
+ *     the tokens that the low-dimensional ranking keeps.
  *   - briefgpt.xyz keyword page (the paper's abstract): tokens in the KV-cache
  *     are ranked and selected by attention scores computed in low-dimensional
  *     space.

@@ -61,9 +61,8 @@ __host__ __device__ __forceinline__ float key_score(unsigned key) {
 // bit is clear (above +inf), bin 0 when it is set (below -inf).
 __host__ __device__ __forceinline__ int lin_bin(float s, float lo, float scale) {
   const float x = (s - lo) * scale;
-  if (x >= (float)(kBins - 1)) return kBins - 1;
-  if (x > 0.f) return (int)x;  // 0 < x < kBins - 1: an exact floor
-  if (x == x || scale == 0.f) return 0;
+  const int b = (int)fminf(fmaxf(x, 0.f), (float)(kBins - 1));  // fmaxf(NaN, 0) is 0
+  if (x == x || scale == 0.f) return b;
   return (__builtin_bit_cast(unsigned, s) & 0x80000000u) ? 0 : kBins - 1;
 }
 
