@@ -101,10 +101,19 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t q0 = (size_t)b * sh.Hq + (size_t)kv * G;  // first query head of the group
 
+  const Rsrc Prs = make_rsrc(p.P + (size_t)kv * D * D, (uint32_t)(D * D * 4));
+  // Phases 0 and 1 are built twice, once per panel cache policy, and a
+  // workgroup takes one: with the policy chosen per load, the compiler could
+  // not tell how many loads were in flight and waited for all of them at
+  // every use (the rotation behind both first batches, every batch behind the
+  // next one).
+  float lo[G], hi[G];
+  float blo = 0.f, bscale = 0.f;  // binning of the single-head histogram
+  auto phase01 = [&](auto keep_tag) {
+  constexpr bool KEEP = decltype(keep_tag)::value;
   // ---- 0. rotation of the panel coordinates: qs[h][0:DP] = q[h] . P[kv][:, 0:DP]
   // Its loads go out first: a wave's loads complete in issue order, so the
   // panel loads issued after them do not delay the rotation.
-  const Rsrc Prs = make_rsrc(p.P + (size_t)kv * D * D, (uint32_t)(D * D * 4));
   const int cql = tid % NQL, rsl = tid / NQL;
   u32x4 pl[NL];
 #pragma unroll
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       const int t = (pass0 + it) * TPP + tl;
       const uint32_t off = t < Ss ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
       // a unit with a helper keeps its panel in L2 for the helper's second read
-      x[it] = paired ? load16(prs, off) : load16_stream(prs, off);
+      x[it] = KEEP ? load16(prs, off) : load16_stream(prs, off);
     }
   };
   u32x4 xa[NB], xb[NB];
@@ -197,8 +206,6 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   // histogram is built as the remaining scores are produced (clamped linear
   // bins stay monotone, whatever the range).  Several heads: the exact range
   // is tracked and the histograms are built after scoring.
-  float lo[G], hi[G];
-  float blo = 0.f, bscale = 0.f;  // binning of the single-head histogram
   {
     float qv[G][E];
 #pragma unroll
@@ -306,16 +313,29 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       if (APPEND && tid == 0 && S - 1 >= NB * TPP)  // the new token, past the first batch
         atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
     }
-    if (2 * NB < n_pass) issue(xa, 2 * NB);
+    // every batch is issued, also past the end (those loads are out of range:
+    // zeros, no memory access), so that the loads in flight are the same on
+    // every path and each use waits only for its own batch; the scheduling
+    // barriers keep each batch's use after the issue of the next one
+    issue(xa, 2 * NB);
+    __builtin_amdgcn_sched_barrier(0);
     consume(xb, NB, true);
-    if (3 * NB < n_pass) issue(xb, 3 * NB);
+    issue(xb, 3 * NB);
+    __builtin_amdgcn_sched_barrier(0);
     for (int pass = 2 * NB; pass < n_pass; pass += 2 * NB) {
       consume(xa, pass, true);
-      if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
+      issue(xa, pass + 2 * NB);
+      __builtin_amdgcn_sched_barrier(0);
       consume(xb, pass + NB, true);
-      if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
+      issue(xb, pass + 3 * NB);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  };
+  if (paired)
+    phase01(std::true_type{});
+  else
+    phase01(std::false_type{});
   if (G > 1) {
 #pragma unroll
     for (int h = 0; h < G; h++) {

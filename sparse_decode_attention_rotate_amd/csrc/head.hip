@@ -120,6 +120,14 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   // the panel is read again by a partner or by sibling heads: keep it in L2
   const bool keep_panel = paired || sh.g > 1;
 
+  // Phases 0 and 1 are built twice, once per panel cache policy, and a
+  // workgroup takes one: with the policy chosen per load, the compiler could
+  // not tell how many loads were in flight and waited for all of them at
+  // every use (the rotation behind both first batches, every batch behind the
+  // next one).
+  float blo = 0.f, bscale = 0.f;  // binning range of the selection histogram
+  auto phase01 = [&](auto keep_tag) {
+  constexpr bool KEEP = decltype(keep_tag)::value;
   __builtin_amdgcn_s_setprio(3);
   // ---- 0. rotation: qs = q . P[kv] (and the new key's row), every column;
   // thread = (column quad cq, row slot rs), rows rs + RSR*u of P
@@ -157,12 +165,15 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
     for (int it = 0; it < NB; it++) {
       const int t = (pass0 + it) * TPP + tl;
       const uint32_t off = t < Ss ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
-      x[it] = keep_panel ? load16(prs, off) : load16_stream(prs, off);
+      x[it] = KEEP ? load16(prs, off) : load16_stream(prs, off);
     }
   };
   u32x4 xa[NB], xb[NB];
+  // with 512 threads a thread holds twice the P rows: the second batch
+  // waits for the rotation, so that the registers suffice
+  constexpr bool kEarlyB = NR <= 4;
   issue(xa, 0);
-  issue(xb, NB);
+  if constexpr (kEarlyB) issue(xb, NB);
 
 #pragma unroll
   for (int u = 0; u < NXV; u++) {
@@ -221,13 +232,13 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       if (tid < D) static_cast<Raw*>(p.vcache)[(head * sh.S_cap + (size_t)(S - 1)) * D + tid] = vraw;
     __syncthreads();
   }
+  if constexpr (!kEarlyB) issue(xb, NB);
 
   __builtin_amdgcn_s_setprio(0);
   // ---- 1b. low-dim scores of every token into LDS, the histogram built as
   // they are produced (after the first batch has fixed the binning range)
   const bool clamp = S > kClampRows;
   float lo = INFINITY, hi = -INFINITY, sum = 0.f, sq = 0.f;
-  float blo = 0.f, bscale = 0.f;
   {
     float qv[E];
 #pragma unroll
@@ -334,16 +345,30 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       if (APPEND && tid == 0 && S - 1 >= NB * TPP)  // the new token, past the first batch
         atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
     }
-    if (2 * NB < n_pass) issue(xa, 2 * NB);
+    // every batch is issued, also past the end (those loads are out of range:
+    // zeros, no memory access), so that the loads in flight are the same on
+    // every path and each use waits only for its own batch
+    // (the scheduling barriers keep each batch's use after the issue of the
+    // next one: hoisted above it, the use would wait for every load)
+    issue(xa, 2 * NB);
+    __builtin_amdgcn_sched_barrier(0);
     consume(xb, NB, true, false);
-    if (3 * NB < n_pass) issue(xb, 3 * NB);
+    issue(xb, 3 * NB);
+    __builtin_amdgcn_sched_barrier(0);
     for (int pass = 2 * NB; pass < n_pass; pass += 2 * NB) {
       consume(xa, pass, true, false);
-      if (pass + 2 * NB < n_pass) issue(xa, pass + 2 * NB);
+      issue(xa, pass + 2 * NB);
+      __builtin_amdgcn_sched_barrier(0);
       consume(xb, pass + NB, true, false);
-      if (pass + 3 * NB < n_pass) issue(xb, pass + 3 * NB);
+      issue(xb, pass + 3 * NB);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  };
+  if (keep_panel)
+    phase01(std::true_type{});
+  else
+    phase01(std::false_type{});
 
   __builtin_amdgcn_s_setprio(3);
   __syncthreads();  // every score is in LDS
