@@ -147,12 +147,18 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
     m = mn;
   };
 
+  // Every batch is issued, also past the last row (those loads are out of
+  // range: zeros, no memory access), so that the loads in flight are the same
+  // on every path and each use waits only for its own batch; the scheduling
+  // barriers keep each batch's use after the issue of the next one.
   u32x4 ka[RB], va[RB], kb2[RB], vb2[RB];
   issue(ka, va, grp);
   for (int base = 0; base < nr; base += ROWS_PER_ITER) {
     issue(kb2, vb2, base + RB * NG + grp);
+    __builtin_amdgcn_sched_barrier(0);
     consume(ka, va, base + grp);
-    if (base + ROWS_PER_ITER < nr) issue(ka, va, base + ROWS_PER_ITER + grp);
+    issue(ka, va, base + ROWS_PER_ITER + grp);
+    __builtin_amdgcn_sched_barrier(0);
     consume(kb2, vb2, base + RB * NG + grp);
   }
 
