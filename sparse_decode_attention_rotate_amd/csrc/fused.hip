@@ -36,6 +36,7 @@
 
 #include "attend_core.h"
 #include "loki_internal.h"
+#include "phase_stamps.h"
 #include "select_core.h"
 
 namespace loki {
@@ -48,6 +49,10 @@ constexpr int kFusedMaxS = 4096;          // scores of a unit held in registers 
 constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per batch
 constexpr size_t kFusedDynBytes = 36 * 1024;
 constexpr int kFusedRowsPerBatch = 4;  // gather rows per lane group per batch
+
+// phase stamps (profiling builds): 0 start, 1 rotation done, 2 scores in
+// LDS, 3 selection (and the rest of the rotation) done, 4 end
+LOKI_STAMP_ARRAY(g_stamps_fused);
 
 template <int DT, int D, int LPT, int G, int NT, bool APPEND>
 __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParams p) {
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   int* sidx = reinterpret_cast<int*>(sc + G * S);        // [G][k]
   float* slow = reinterpret_cast<float*>(sidx + G * k);  // [G][k]
 
+  LOKI_STAMP(g_stamps_fused, 0);
+  LOKI_STAMP_HWID(g_stamps_fused);
   // Wave priority: the short latency-bound phases (rotation, top-k) run at
   // high priority so that they are not starved of issue slots by the
   // streaming phases of co-resident workgroups; streaming runs at the lowest.
@@ -200,6 +207,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   }
   __syncthreads();
 
+  LOKI_STAMP(g_stamps_fused, 1);
   __builtin_amdgcn_s_setprio(0);
   // ---- 1b. low-dim scores of every token into LDS.  Single head: the
   // scores of the first batch fix a provisional binning range, the select
@@ -350,6 +358,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       }
   }
 
+  LOKI_STAMP(g_stamps_fused, 2);
   __builtin_amdgcn_s_setprio(3);
   // ---- 0'. the rest of the rotation: its P loads stay in flight through the top-k
   const int cqr = tid % 32, rsr = tid / 32;
@@ -451,6 +460,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     __syncthreads();
   }
 
+  LOKI_STAMP(g_stamps_fused, 3);
   __builtin_amdgcn_s_setprio(0);
   // ---- 3. exact attention over the selected tokens of each head
   // (the index sets, when asked for, are written after it: off its critical path)
@@ -499,6 +509,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
                 sh.odt);
     }
     write_idx();
+    LOKI_STAMP(g_stamps_fused, 4);
     return;
   }
   for (int h = 0; h < G; h++) {
@@ -509,6 +520,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
     __syncthreads();  // asm_ is reused by the next head
   }
   write_idx();
+  LOKI_STAMP(g_stamps_fused, 4);
 }
 
 template <int DT, int D, int LPT, int NT, bool APPEND>
@@ -564,3 +576,5 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t st) {
 }
 
 }  // namespace loki
+
+LOKI_STAMP_EXPORT(loki_phase_stamps_fused, loki::g_stamps_fused);

@@ -40,6 +40,7 @@
 
 #include "attend_core.h"
 #include "loki_internal.h"
+#include "phase_stamps.h"
 #include "select_core.h"
 
 namespace loki {
@@ -71,6 +72,10 @@ struct HeadLds {
     return sc > e ? (sc > q ? sc : q) : (e > q ? e : q);
   }
 };
+
+// phase stamps (profiling builds): 0 start, 1 rotation done, 2 scores in
+// LDS, 3 selection done, 4 attention starts, 5 end
+LOKI_STAMP_ARRAY(g_stamps_head);
 
 template <int DT, int D, int LPT, int NT, int KREG, bool APPEND>
 __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
@@ -126,6 +131,8 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   // every use (the rotation behind both first batches, every batch behind the
   // next one).
   float blo = 0.f, bscale = 0.f;  // binning range of the selection histogram
+  LOKI_STAMP(g_stamps_head, 0);
+  LOKI_STAMP_HWID(g_stamps_head);
   auto phase01 = [&](auto keep_tag) {
   constexpr bool KEEP = decltype(keep_tag)::value;
   __builtin_amdgcn_s_setprio(3);
@@ -234,6 +241,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   }
   if constexpr (!kEarlyB) issue(xb, NB);
 
+  LOKI_STAMP(g_stamps_head, 1);
   __builtin_amdgcn_s_setprio(0);
   // ---- 1b. low-dim scores of every token into LDS, the histogram built as
   // they are produced (after the first batch has fixed the binning range)
@@ -372,6 +380,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
 
   __builtin_amdgcn_s_setprio(3);
   __syncthreads();  // every score is in LDS
+  LOKI_STAMP(g_stamps_head, 2);
 
   // ---- 2. top-k: the scores as order keys in registers, then the LDS reused
   int* sidx = reinterpret_cast<int*>(reuse);                   // [k]
@@ -395,6 +404,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
                                      p.idx_out + (size_t)bh * k);
     }
   }
+  LOKI_STAMP(g_stamps_head, 3);
   if constexpr (APPEND) {
     // the gathers may read row S-1: this wave's stores of it are complete
     // before the barrier that follows
@@ -402,6 +412,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   }
   __syncthreads();
 
+  LOKI_STAMP(g_stamps_head, 4);
   __builtin_amdgcn_s_setprio(0);
   // ---- 3. exact attention over the selected tokens
   const int r0 = paired && helper ? p.k0 : 0;
@@ -442,6 +453,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   } else if (tid < D) {
     store_out(p.out, (size_t)bh * D + tid, A / Lsum, sh.odt);
   }
+  LOKI_STAMP(g_stamps_head, 5);
 }
 
 // Threads per workgroup for rows of S tokens: 512 (two workgroups per
@@ -536,3 +548,5 @@ hipError_t launch_head(const HeadParams& p, hipStream_t st) {
 }
 
 }  // namespace loki
+
+LOKI_STAMP_EXPORT(loki_phase_stamps_head, loki::g_stamps_head);
