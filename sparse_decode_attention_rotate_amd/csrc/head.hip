@@ -84,7 +84,10 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   constexpr int E = Elem<DT>::kPerVec;
   constexpr int DP = LPT * 16 / Elem<DT>::kBytes;  // panel width (== d)
   constexpr int TPP = NT / LPT;                    // tokens per pass over the panel
-  constexpr int NB = kHeadBatch;
+  // 512 threads (a thread holds 8 rows of P during the rotation): batches of
+  // 4 loads, so that nothing spills (a spill reload waits for every load in
+  // flight)
+  constexpr int NB = NT >= 1024 ? kHeadBatch : kHeadBatch / 2;
   // rotation: 32 column quads x NT/32 row slots (D/4 <= 32 quads in use)
   constexpr int RSR = NT / 32, NR = (D + RSR - 1) / RSR;
   constexpr int NXV = (GR * D + NT - 1) / NT;
@@ -176,9 +179,10 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
     }
   };
   u32x4 xa[NB], xb[NB];
-  // with 512 threads a thread holds twice the P rows: the second batch
-  // waits for the rotation, so that the registers suffice
-  constexpr bool kEarlyB = NR <= 4;
+  // both batches in flight during the rotation while the P rows and the
+  // batches fit 80 registers (1024 threads: 4 rows of P and two batches of 8
+  // loads; 512 threads: 8 rows and two batches of 4)
+  constexpr bool kEarlyB = NR * 4 + 2 * NB * 4 <= 80;
   issue(xa, 0);
   if constexpr (kEarlyB) issue(xb, NB);
 
