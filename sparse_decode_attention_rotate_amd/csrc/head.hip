@@ -18,10 +18,9 @@
 //     scores do not crowd the bulk into few bins) and every later score is
 //     added to the selection histogram as it is produced;
 //  2. the scores become order keys in registers, the LDS that held them is
-//     reused, and select_keys (select_core.h) writes the selected tokens and
-//     their low-dim partial logits (each lane its own in turn: not in index
-//     order, which the attention does not need; the index set, when asked
-//     for, is written in ascending order from a bitmap of the taken tokens);
+//     reused, and select_keys (select_core.h) writes the selected tokens, in
+//     ascending order, and their low-dim partial logits (the index set, when
+//     asked for, is a copy of that list);
 //  3. block_attend (attend_core.h) gathers the selected key tails and value
 //     rows.
 // Grouped query heads: the g heads of one (b, kv) are g workgroups on one XCD
@@ -56,10 +55,8 @@ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 // Byte offsets inside the reused LDS region, once the scores are in registers:
 // selected tokens [k] i32, their partial logits [k] f32, the radix passes'
-// per-wave histograms (then the bitmap of the index output), the attention's
-// merge (first the selection's per-lane counts).  Before that the region
-// holds the row of scores, and before those the rotation's per-wave partial
-// sums.
+// per-wave histograms, the attention's merge.  Before that the region holds
+// the row of scores, and before those the rotation's per-wave partial sums.
 template <int DT, int D, int NT, int GR>
 struct HeadLds {
   static constexpr int NW = NT / 64;
@@ -396,17 +393,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
     auto ld = [&](int i) -> float { return i < S ? sc[i] : __uint_as_float(0xffffffffu); };
     RowView<NT, KREG, decltype(ld)> row(ld, S);
     __syncthreads();  // every key is in registers: the scores' LDS is free
-    // per-lane counts of select_keys in the attention's (not yet used) LDS
-    select_keys<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, whist,
-                          reinterpret_cast<int*>(&asm_));
-    if (p.idx_out && !helper) {
-      // the index set in ascending order (only when asked for): a bitmap of
-      // the taken elements in the radix histograms' LDS, then its set bits
-      __syncthreads();
-      write_taken_in_order<NT, KREG>(row, ssm, reinterpret_cast<unsigned long long*>(whist),
-                                     reinterpret_cast<int*>(whist) + 2 * ((S + 63) / 64),
-                                     p.idx_out + (size_t)bh * k);
-    }
+    select_keys<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, whist);
   }
   LOKI_STAMP(g_stamps_head, 3);
   if constexpr (APPEND) {
@@ -415,6 +402,9 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
     wait_stores();
   }
   __syncthreads();
+  // the index set, when asked for: the selected list is in ascending order
+  if (p.idx_out && !helper)
+    for (int e = tid; e < k; e += NT) p.idx_out[(size_t)bh * k + e] = sidx[e];
 
   LOKI_STAMP(g_stamps_head, 4);
   __builtin_amdgcn_s_setprio(0);

@@ -496,34 +496,33 @@ __device__ __forceinline__ unsigned long long first_key_of_bin(unsigned long lon
 //    linear sub-bins (one pass over the interval's keys and a scan) and the
 //    interval narrowed to the sub-bin holding the k-th score; radix passes
 //    over the interval's keys resolve a group still crowded after that;
-//  * one pass counts, per lane, the keys above the interval and marks the
-//    interval's keys (a bit per key, registers only); the marked candidates
+//  * one pass counts, per wave, the keys above the interval and marks the
+//    interval's keys (a bit per key, registers only); each wave copies its
+//    marked candidates to LDS at slots it reserves at once; the candidates
 //    are ranked by (key descending, index ascending) and the rem first are
 //    taken; (T, I) is the last taken;
 //  * one pass writes the taken elements: element i with key > T, or
-//    key == T and i <= I.  Each lane writes its own ones consecutively from
-//    an offset given by the counts of the waves and lanes before it, so the
-//    output is ordered by (wave, lane, element of the lane), not by index;
-//    the order is a function of the keys alone (deterministic).
+//    key == T and i <= I.  Key slot j of a wave holds 64 consecutive
+//    indices, so one ballot per slot places them after the counts of the
+//    waves and ballots before: the output is in ascending index order.
 // Padding elements (index >= S) must have key 0 (load_score gives them the
 // all-ones NaN) and no score may have those bits: key 0 is then never taken
 // and no pass checks the index.  sm.hist holds the histogram under
-// (lo, scale) and sm.n_cand is 0; lane_extra: NT ints of LDS; whist: the
-// radix passes' per-wave histograms.  Writes k entries of out_idx / out_val
-// (the taken indices and their scores, -0 as +0) and sm.thr_key /
-// sm.thr_idx = (T, I).  All NT threads; the caller needs a barrier before
-// reading the output.
+// (lo, scale) and sm.n_cand is 0; whist: the radix passes' per-wave
+// histograms.  Writes k entries of out_idx / out_val (the taken indices, in
+// ascending order, and their scores, -0 as +0) and sm.thr_key / sm.thr_idx =
+// (T, I).  All NT threads; the caller needs a barrier before reading the
+// output.
 template <int NT, int KREG, typename Load, typename SM>
 __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k, int32_t* out_idx,
                                             float* out_val, SM& sm, float lo, float scale,
-                                            unsigned (*whist)[256], int* lane_extra) {
+                                            unsigned (*whist)[256]) {
   constexpr int NW = NT / 64;
   static_assert(NW >= 2, "two waves search the interval's ends");
   static_assert(KREG > 0 && KREG <= 32, "keys in registers, a bit per key of a thread");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  lane_extra[tid] = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  select_scan<NT>(sm, k);  // ends with a barrier (lane_extra is zero)
+  select_scan<NT>(sm, k);  // ends with a barrier
   const int bstar = sm.sel_bin;
   const int rem0 = k - sm.sel_gt;  // 1 <= rem0 <= members of b*
   int rem = rem0, nb = sm.sel_eq;
@@ -544,7 +543,7 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
   // ---- a crowded b*: linear sub-bins of its interval
   if (nb > kFewCandidates && scale > 0.f && scale * (float)kBins < INFINITY) {
     const float lo2 = lo + (float)bstar / scale, scale2 = scale * (float)kBins;
-    for (int e = tid; e < kBins; e += NT) sm.hist[e] = 0u;
+    for (int e = (int)threadIdx.x; e < kBins; e += NT) sm.hist[e] = 0u;
     __syncthreads();  // every thread has read the first scan's results
 #pragma unroll
     for (int j = 0; j < KREG; j++) {
@@ -571,8 +570,7 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
     khi1 = sm.key_hi1;
   }
 
-  // ---- the last taken element (T, I) and each lane's number of taken ones
-  unsigned mine;  // this lane's taken elements, but for taken candidates
+  // ---- the last taken element (T, I) and each wave's number of taken ones
   if (nb <= kFewCandidates) {
     unsigned gt = 0u, cmask = 0u;
     const unsigned span = khi1 - klo;  // key - klo <= span: klo <= key <= khi1
@@ -582,14 +580,25 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
       gt += key > khi1 ? 1u : 0u;
       cmask |= (key - klo <= span) ? (1u << j) : 0u;
     }
-    mine = gt;
     if (__ballot(cmask != 0u) != 0ull) {  // rare: this wave holds members of the group
+      // the wave's candidates take consecutive slots: one reservation, then
+      // a ballot per key slot (at most kFewCandidates in all: the group's
+      // members are exactly the nb elements its bin counted)
+      const int nc = (int)wave_sum((float)__popc(cmask));  // exact: at most 64 * KREG
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&sm.n_cand, nc);
+      slot = __shfl(slot, 0, 64);
 #pragma unroll
       for (int j = 0; j < KREG; j++) {
-        if (cmask & (1u << j)) {
-          const int slot = atomicAdd(&sm.n_cand, 1);
-          sm.cand_key[slot] = row.kv[j];
-          sm.cand_idx[slot] = row.base + j * 64;
+        const bool c = (cmask >> j) & 1u;
+        const unsigned long long m = __ballot(c);
+        if (m != 0ull) {
+          if (c) {
+            const int at = slot + lane_rank(m);
+            sm.cand_key[at] = row.kv[j];
+            sm.cand_idx[at] = row.base + j * 64;
+          }
+          slot += __popcll(m);
         }
       }
     }
@@ -598,8 +607,8 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
     __syncthreads();
     // rank of candidate c = members ordered before it by (key descending,
     // index ascending): one ballot over the candidates on the lanes; the
-    // waves take the candidates in turn; a taken one counts for its wave and
-    // its lane (element i sits on thread (i / per_wave) * 64 + i % 64)
+    // waves take the candidates in turn; a taken one counts for its wave
+    // (element i sits in wave i / per_wave)
     {
       const bool have = lane < nb;
       const unsigned mk = have ? sm.cand_key[lane] : 0u;
@@ -613,11 +622,7 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
             sm.thr_key = ck;
             sm.thr_idx = ci;
           }
-          if (rank < rem) {
-            const int w = ci / row.per_wave;
-            atomicAdd(&sm.wcnt[w], 1);
-            atomicAdd(&lane_extra[w * 64 + ci % 64], 1);
-          }
+          if (rank < rem) atomicAdd(&sm.wcnt[ci / row.per_wave], 1);
         }
       }
     }
@@ -633,73 +638,29 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
       const unsigned key = row.kv[j];
       cnt += (key > T || (key == T && row.base + j * 64 <= I)) ? 1u : 0u;
     }
-    mine = cnt;
     cnt = (unsigned)wave_sum((float)cnt);
     if (lane == 0) sm.wcnt[wave] = (int)cnt;
     __syncthreads();
   }
 
-  // ---- write the taken elements, each lane its own consecutively
+  // ---- write the taken elements: key slot j of a wave holds 64 consecutive
+  // indices, so a ballot per slot writes them in ascending index order
   const unsigned T = sm.thr_key;
   const int I = sm.thr_idx;
-  const unsigned own = mine + (unsigned)lane_extra[tid];
-  int out = (int)(wave_incl_scan(own) - own);
+  int out = 0;
   for (int w = 0; w < wave; w++) out += sm.wcnt[w];
 #pragma unroll
   for (int j = 0; j < KREG; j++) {
     const unsigned key = row.kv[j];
     const int i = row.base + j * 64;
-    if (key > T || (key == T && i <= I)) {
-      out_idx[out] = i;
-      out_val[out] = key_score(key);
-      out++;
+    const bool take = key > T || (key == T && i <= I);
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      const int at = out + lane_rank(m);
+      out_idx[at] = i;
+      out_val[at] = key_score(key);
     }
-  }
-}
-
-// The taken elements of select_keys (same keys, same (T, I) in sm) as a
-// bitmap, then their indices in ascending order to `dst` (global memory).
-// bits: S/64 + 1 words of LDS; scan: NT/64 ints of LDS.  All NT threads.
-template <int NT, int KREG, typename Load, typename SM>
-__device__ __forceinline__ void write_taken_in_order(RowView<NT, KREG, Load>& row, SM& sm,
-                                                     unsigned long long* bits, int* scan,
-                                                     int32_t* dst) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned T = sm.thr_key;
-  const int I = sm.thr_idx;
-  // element i = wave * per_wave + j * 64 + lane: word (wave * per_wave) / 64 + j
-  const int words = (row.S + 63) / 64;
-#pragma unroll
-  for (int j = 0; j < KREG; j++) {
-    const unsigned key = row.kv[j];
-    const int i = row.base + j * 64;
-    const unsigned long long m = __ballot(key > T || (key == T && i <= I));
-    const int wd = (wave * row.per_wave) / 64 + j;
-    if (lane == 0 && wd < words) bits[wd] = m;
-  }
-  __syncthreads();
-  // word w to thread w (and w + NT, ...): counts, a block scan, the indices
-  int pre = 0;
-  for (int w0 = 0; w0 < words; w0 += NT) {
-    const int w = w0 + tid;
-    const unsigned long long m = w < words ? bits[w] : 0ull;
-    const unsigned c = (unsigned)__popcll(m);
-    const unsigned incl = wave_incl_scan(c);
-    if (lane == 63) scan[wave] = (int)incl;
-    __syncthreads();
-    int base = pre + (int)(incl - c);
-    for (int v = 0; v < wave; v++) base += scan[v];
-    int tot = 0;
-    for (int v = 0; v < NW; v++) tot += scan[v];
-    unsigned long long r = m;
-    while (r != 0ull) {
-      const int bit = __builtin_ctzll(r);
-      dst[base++] = w * 64 + bit;
-      r &= r - 1ull;
-    }
-    pre += tot;
-    __syncthreads();  // scan is reused by the next block of words
+    out += __popcll(m);
   }
 }
 
