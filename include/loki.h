@@ -119,6 +119,20 @@ typedef struct {
    cleared by the second of the two. */
 #define LOKI_FLAG_NO_HELPERS 2u
 
+/* loki_desc.flags: in the one-launch kernel with one query head per
+   workgroup, a head and its helper each stream the whole panel.  By default
+   (rows of at least four load batches per half) each streams one half of the
+   panel and the two hand their scores to each other through the workspace,
+   so the panel is read once, with the nontemporal policy.  Same results, bit
+   for bit. */
+#define LOKI_FLAG_NO_SHARED_STREAM 4u
+
+/* loki_desc.flags, for testing: the two workgroups sharing a stream do not
+   wait for each other; a half that is not published when it is needed is
+   scored by the workgroup that needs it (the path a workgroup takes when
+   its partner is not resident within 20 us).  Same results, bit for bit. */
+#define LOKI_FLAG_SHARED_NO_WAIT 8u
+
 /* Human-readable name of a status code; never NULL. */
 const char* loki_strerror(int status);
 
@@ -139,9 +153,9 @@ int loki_workspace_bytes(const loki_desc* desc, int d, int k, size_t* bytes);
  * (b, kv) with its group's scores in LDS (head_dim 128, Hq/Hkv in {1, 2, 4},
  * S <= 4096, the group's scores and index lists within the LDS budget).
  * 2: otherwise, up to S = 32768: one workgroup per query head with its whole
- * row of scores in LDS (plus helper workgroups sharing the heads' attention
- * when the heads leave compute units free).  The plan is the same with or
- * without append.
+ * row of scores in LDS (plus helper workgroups sharing the heads' panel
+ * stream and attention when the heads leave compute units free).  The plan
+ * is the same with or without append.
  */
 int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_launch);
 

@@ -70,8 +70,34 @@ struct HeadLds {
   }
 };
 
+// Polls a flag until it holds tag, for at most `ticks` of the constant
+// 100 MHz clock; true when it did.
+__device__ __forceinline__ bool wait_flag(const unsigned long long* f, unsigned long long tag,
+                                          unsigned long long ticks) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  return true;
+}
+
+// A member of a pair sharing the stream is through with the hand-over (its
+// half published, the other half read or scored itself).  xf[0], xf[1]: the
+// members' flags; xf[2]: the tag of the first member through.  The second
+// clears all three, so that a replay of a captured launch, which reuses the
+// tag, starts afresh.
+__device__ __forceinline__ void pair_share_done(unsigned long long* xf, unsigned long long tag) {
+  if (__hip_atomic_exchange(xf + 2, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) {
+    __hip_atomic_store(xf + 0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(xf + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(xf + 2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // phase stamps (profiling builds): 0 start, 1 rotation done, 2 scores in
-// LDS, 3 selection done, 4 attention starts, 5 end
+// LDS, 3 selection done, 4 attention starts, 5 end, 6 own half of the
+// scores done (pairs sharing the stream)
 LOKI_STAMP_ARRAY(g_stamps_head);
 
 template <int DT, int D, int LPT, int NT, int KREG, bool APPEND>
@@ -98,6 +124,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   __shared__ float kn[APPEND ? D : 1];  // rotated new key as stored
   __shared__ float rng[4][NW];          // per-wave min, max, sum, sum of squares
   __shared__ int later;                 // paired head: this workgroup merges the halves
+  __shared__ int xok;                   // shared stream: the partner's half has arrived
 
   const Shape& sh = p.sh;
   const int S = sh.S, k = p.k;
@@ -122,19 +149,32 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   const bool paired = sh.g == 1 && p.n_help > 0 && pair >= 0 && pair < p.n_help;
   const int b = bh / sh.Hq, kv = (bh % sh.Hq) / sh.g;
   const size_t head = (size_t)b * sh.Hkv + kv;  // (b, kv) block of the caches
+  // A head and its helper share out the stream (p.share): each streams one
+  // half of the passes and hands its scores to the other through the
+  // workspace.  Otherwise each streams the whole panel.
+  const bool share = paired && p.share;
+  const int member = helper ? 1 : 0;
+  const int n_pass_all = (Ss + TPP - 1) / TPP;
+  const int half = n_pass_all / 2;  // member 0: passes [0, half), member 1: the rest
+  const int pass_lo = share && member ? half : 0;
+  const int n_pass = share ? (member ? n_pass_all - half : half) : n_pass_all;
+  const int t_lo = pass_lo * TPP, t_hi = min((pass_lo + n_pass) * TPP, Ss);
   // the panel is read again by a partner or by sibling heads: keep it in L2
-  const bool keep_panel = paired || sh.g > 1;
+  const bool keep_panel = (paired && !share) || sh.g > 1;
 
-  // Phases 0 and 1 are built twice, once per panel cache policy, and a
-  // workgroup takes one: with the policy chosen per load, the compiler could
-  // not tell how many loads were in flight and waited for all of them at
-  // every use (the rotation behind both first batches, every batch behind the
-  // next one).
+  // Phases 0 and 1 are built three times (the panel kept in L2; streamed
+  // with the nontemporal policy; streamed and shared) and a workgroup takes
+  // one: with the policy or the hand-over's stores chosen per load, the
+  // compiler could not tell how many loads were in flight and waited for all
+  // of them at every use (the rotation behind both first batches, every
+  // batch behind the next one).
   float blo = 0.f, bscale = 0.f;  // binning range of the selection histogram
+  float* const xrow = share ? p.xbuf + (size_t)bh * S : nullptr;  // scores handed over
   LOKI_STAMP(g_stamps_head, 0);
   LOKI_STAMP_HWID(g_stamps_head);
-  auto phase01 = [&](auto keep_tag) {
+  auto phase01 = [&](auto keep_tag, auto share_tag) {
   constexpr bool KEEP = decltype(keep_tag)::value;
+  constexpr bool SHARE = decltype(share_tag)::value;
   __builtin_amdgcn_s_setprio(3);
   // ---- 0. rotation: qs = q . P[kv] (and the new key's row), every column;
   // thread = (column quad cq, row slot rs), rows rs + RSR*u of P
@@ -166,12 +206,11 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   const Rsrc prs = make_rsrc(static_cast<const char*>(p.kcache) +
                                  head * sh.kl.head_elems * (size_t)Elem<DT>::kBytes,
                              (uint32_t)((size_t)sh.S_cap * LPT * 16));
-  const int n_pass = (S + TPP - 1) / TPP;
   auto issue = [&](u32x4 (&x)[NB], int pass0) {
 #pragma unroll
     for (int it = 0; it < NB; it++) {
-      const int t = (pass0 + it) * TPP + tl;
-      const uint32_t off = t < Ss ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
+      const int t = (pass_lo + pass0 + it) * TPP + tl;
+      const uint32_t off = t < t_hi ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange;
       x[it] = KEEP ? load16(prs, off) : load16_stream(prs, off);
     }
   };
@@ -268,7 +307,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
         }
       }
     }
-    // a finished score r of token t (t < Ss)
+    // a finished score r of token t (t_lo <= t < t_hi)
     auto put = [&](int t, float r, bool hist, bool first) {
       if (first) {
         lo = fminf(lo, r);
@@ -300,8 +339,8 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
           const float u0 = (b0 ? a[g0 + 1] : a[g0]) + dpp_f<0xB1>(b0 ? a[g0] : a[g0 + 1]);
           const float u1 = (b0 ? a[g0 + 3] : a[g0 + 2]) + dpp_f<0xB1>(b0 ? a[g0 + 2] : a[g0 + 3]);
           const float r = (b1 ? u1 : u0) + dpp_f<0x4E>(b1 ? u0 : u1);
-          const int t = (pass0 + g0 + c) * TPP + tl;
-          if (t < Ss) put(t, r, hist, first);
+          const int t = (pass_lo + pass0 + g0 + c) * TPP + tl;
+          if (t < t_hi) put(t, r, hist, first);
         }
       } else {
 #pragma unroll
@@ -312,8 +351,8 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
 #pragma unroll
           for (int e = 0; e < E; e++) a = fmaf(qv[e], f[e], a);
           a = group_sum<LPT>(a);
-          const int t = (pass0 + it) * TPP + tl;
-          if (t < Ss && c == 0) put(t, a, hist, first);
+          const int t = (pass_lo + pass0 + it) * TPP + tl;
+          if (t < t_hi && c == 0) put(t, a, hist, first);
         }
       }
     };
@@ -342,16 +381,16 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
         // mean +- 6 sd of the first batch, within its min / max; scores
         // outside land in the end bins (clamped bins stay monotone); a
         // non-finite mean or spread leaves the range as it is
-        const float n1 = (float)min(Ss, NB * TPP);
+        const float n1 = (float)min(t_hi - t_lo, NB * TPP);
         const float mean = s1 / n1;
         const float sd = sqrtf(fmaxf(s2 / n1 - mean * mean, 0.f));
         blo = fmaxf(blo, mean - 6.f * sd);
         bhi = fminf(bhi, mean + 6.f * sd);
       }
       bscale = bin_scale(blo, bhi);
-      for (int t = tid; t < min(S, NB * TPP); t += NT)
+      for (int t = t_lo + tid; t < min(t_hi, t_lo + NB * TPP); t += NT)
         atomicAdd(&ssm.hist[lin_bin(sc[t], blo, bscale)], 1u);
-      if (APPEND && tid == 0 && S - 1 >= NB * TPP)  // the new token, past the first batch
+      if (APPEND && tid == 0)  // the new token (never streamed)
         atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
     }
     // every batch is issued, also past the end (those loads are out of range:
@@ -372,12 +411,84 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       issue(xb, pass + 3 * NB);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (SHARE) {
+      // ---- 1c. the hand-over: this half of the row goes out through the
+      // workspace (agent-coherent words), the other half comes in.  The
+      // stores wait for the end of the stream: issued among its loads, or by
+      // waves already through it, they slowed the stream down by more than
+      // they saved (measured)
+      LOKI_STAMP(g_stamps_head, 6);
+      __syncthreads();  // this half's scores are in LDS
+      for (int t = t_lo + tid; t < t_hi; t += NT) st_coherent(xrow + t, sc[t]);
+      wait_stores();
+      __syncthreads();  // every store of this half is complete
+      unsigned long long* xf = p.xflag + (size_t)pair * 4;
+      if (tid == 0) {
+        __hip_atomic_store(xf + member, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        xok = wait_flag(xf + (1 - member), p.tag, p.wait_ticks);
+      }
+      __syncthreads();
+      const int u_lo = member ? 0 : half * TPP, u_hi = member ? half * TPP : Ss;
+      if (xok) {
+        // 16-byte agent-coherent loads (sc1), four in flight per thread, over
+        // the 16-byte quads that hold the half (quads counted from the
+        // 16-byte boundary at or below the row's start; words outside the
+        // half are not used)
+        const int sft = (int)(((size_t)bh * S) & 3);
+        const Rsrc xr = make_rsrc(xrow - sft, (uint32_t)((S + sft) * 4));
+        const int q_lo = (u_lo + sft) >> 2, q_hi = (u_hi + sft + 3) >> 2;
+        for (int q0 = q_lo + tid; q0 < q_hi; q0 += 4 * NT) {
+          u32x4 r[4];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int qi = q0 + q * NT;
+            r[q] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           xr, qi < q_hi ? (int)(16 * qi) : (int)kOutOfRange, 0, kCoherentSc1));
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const int t = 4 * (q0 + q * NT) + e - sft;
+              if (t >= u_lo && t < u_hi) {
+                const float v = __uint_as_float(r[q][e]);
+                sc[t] = v;
+                atomicAdd(&ssm.hist[lin_bin(v, blo, bscale)], 1u);
+              }
+            }
+          }
+        }
+      } else {
+        // the partner has not published in time (not resident yet): its
+        // half is scored here, with the same sums (group_sum adds the lanes'
+        // partials as the stream's reduce-scatter does)
+        for (int pass = u_lo / TPP; pass * TPP < u_hi; pass++) {
+          const int t = pass * TPP + tl;
+          const u32x4 x =
+              load16_stream(prs, t < u_hi ? ((uint32_t)t * LPT + c) * 16 : kOutOfRange);
+          float f[E];
+          unpack16<DT>(x, f);
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; e++) a = fmaf(qv[e], f[e], a);
+          a = group_sum<LPT>(a);
+          if (c == 0 && t < u_hi) {
+            sc[t] = a;
+            atomicAdd(&ssm.hist[lin_bin(a, blo, bscale)], 1u);
+          }
+        }
+      }
+      if (tid == 0) pair_share_done(xf, p.tag);
+    }
   }
   };
-  if (keep_panel)
-    phase01(std::true_type{});
+  if (share)
+    phase01(std::false_type{}, std::true_type{});
+  else if (keep_panel)
+    phase01(std::true_type{}, std::false_type{});
   else
-    phase01(std::false_type{});
+    phase01(std::false_type{}, std::false_type{});
 
   __builtin_amdgcn_s_setprio(3);
   __syncthreads();  // every score is in LDS
@@ -516,6 +627,14 @@ size_t lds_dt(const Shape& sh, int k) {
 }  // namespace
 
 int head_kernel_threads(const Shape& sh) { return head_threads(sh.S); }
+
+bool head_share_ok(const Shape& sh, int streamed) {
+  const int nt = head_threads(sh.S);
+  const int lpt = sh.dp * (sh.dtype == F32 ? 4 : 2) / 16;
+  const int nb = nt >= 1024 ? kHeadBatch : kHeadBatch / 2;
+  const int passes = (streamed + nt / lpt - 1) / (nt / lpt);
+  return passes >= 4 * nb;
+}
 
 bool head_supported(const Shape& sh, int d, int k) {
   const int eb = sh.dtype == F32 ? 4 : 2;

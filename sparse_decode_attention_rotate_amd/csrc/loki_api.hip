@@ -98,7 +98,7 @@ int check_desc(const loki_desc* d, Shape* sh) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qr, scores, idx, sel, part, help_flag, help_part, total;
+  size_t qr, scores, idx, sel, part, help_flag, help_part, xflag, total;
   int nsplit;
 };
 
@@ -124,6 +124,11 @@ WsLayout ws_layout(const Shape& sh, int k) {
   off += align256(kv_units * 8);
   w.help_part = off;
   off += align256(kv_units * 2 * (size_t)(sh.D + 2) * 4);
+  // pairs of the one-head-per-workgroup kernel sharing the stream: four
+  // words per pair (at most one pair per query head); the scores handed over
+  // go through the scores region
+  w.xflag = off;
+  off += align256(units * 4 * 8);
   w.total = off;
   return w;
 }
@@ -297,6 +302,16 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
         hp.help_part = reinterpret_cast<float*>(ws + w.help_part);
         hp.help_flag = reinterpret_cast<unsigned long long*>(ws + w.help_flag);
         hp.tag = next_tag(workspace);
+        // a head and its helper stream one half of the panel each and hand
+        // the scores over (every workgroup is resident at once: heads +
+        // helpers <= slots)
+        if (!(desc->flags & LOKI_FLAG_NO_SHARED_STREAM) &&
+            head_share_ok(sh, append ? sh.S - 1 : sh.S)) {
+          hp.share = 1;
+          hp.xbuf = reinterpret_cast<float*>(ws + w.scores);
+          hp.xflag = reinterpret_cast<unsigned long long*>(ws + w.xflag);
+          hp.wait_ticks = (desc->flags & LOKI_FLAG_SHARED_NO_WAIT) ? 0ull : kShareWaitTicks;
+        }
       }
     } else {
       // the g heads of a (b, kv) on one XCD: whole blocks of 8 (b, kv) units

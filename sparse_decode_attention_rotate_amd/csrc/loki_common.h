@@ -210,6 +210,9 @@ __device__ __forceinline__ float ld_coherent(const float* a) {
                                            __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// cache policy of a buffer access with the agent-coherent bit (sc1), as the
+// agent-scope accesses above: for 16-byte loads of words stored that way
+constexpr int kCoherentSc1 = 16;
 
 // ---------------------------------------------------------------- K cache layout
 //

@@ -107,6 +107,12 @@ struct HeadParams {
   float* help_part;     // [n_help][2][D + 2] partials (coherent accesses only)
   unsigned long long* help_flag;  // [n_help] launch tag of the first half done
   unsigned long long tag;         // unique per launch on one workspace, nonzero
+  // a head and its helper sharing out the panel stream: each streams one
+  // half of the passes and hands its scores over
+  int share;                      // 1: the pairs share the stream
+  float* xbuf;                    // [B*Hq][S] scores handed over (coherent accesses only)
+  unsigned long long* xflag;      // [n_help][4] members' flags (tag), the first through at 2
+  unsigned long long wait_ticks;  // longest wait for the partner's half (100 MHz clock)
   Shape sh;
 };
 
@@ -161,6 +167,10 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t st);
 // does not take.
 bool head_supported(const Shape& sh, int d, int k);
 int head_kernel_threads(const Shape& sh);
+// whether a head and its helper share out the stream of a row of `streamed`
+// panel rows (each half at least two load batches)
+bool head_share_ok(const Shape& sh, int streamed);
+constexpr unsigned long long kShareWaitTicks = 2000;  // 20 us of the 100 MHz clock
 hipError_t launch_head(const HeadParams& p, hipStream_t st);
 
 // Rows of the selected set processed by one attention workgroup.

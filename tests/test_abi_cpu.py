@@ -50,7 +50,8 @@ def test_library_exports_every_declared_symbol(L):
 def test_header_flags_match_binding(L):
     src = open(HEADER).read()
     flags = dict(re.findall(r"#define\s+LOKI_(FLAG_\w+)\s+(\d+)u", src))
-    assert flags == {"FLAG_SEPARATE_KERNELS": "1", "FLAG_NO_HELPERS": "2"}
+    assert flags == {"FLAG_SEPARATE_KERNELS": "1", "FLAG_NO_HELPERS": "2",
+                     "FLAG_NO_SHARED_STREAM": "4", "FLAG_SHARED_NO_WAIT": "8"}
     for name, v in flags.items():
         assert getattr(L, name) == int(v)
 

@@ -764,6 +764,74 @@ def test_helpers_match_solo_units(L, dtype, B, nh, S, k):
     H.log(f"  helpers {dtype} B={B} heads={nh}: {res}")
 
 
+# A head and its helper share out the panel stream (default): each streams one
+# half of the passes and the two hand their scores over through the
+# workspace; a half not published in time is scored by the member needing it.
+SHARED_CASES = {
+    "bf16-20000-heavy": dict(dtype="bf16", B=2, Hq=8, Hkv=8, S=20000, k=2500, heavy_frac=0.02),
+    "f16-512thr-ragged": dict(dtype="f16", B=1, Hq=8, Hkv=8, S=12345, k=1234),
+    "bf16-32768-append": dict(dtype="bf16", B=1, Hq=8, Hkv=8, S=32768, S_cap=32768, k=4096,
+                              append=True),
+    "f16-d96-append": dict(dtype="f16", B=1, Hq=8, Hkv=8, D=96, S=9001, S_cap=9100, k=900,
+                           append=True),
+    "f32-lpt8": dict(dtype="f32", B=1, Hq=8, Hkv=8, S=6000, k=700, tau=20.0),
+}
+
+
+@pytest.mark.parametrize("case", list(SHARED_CASES), ids=list(SHARED_CASES))
+def test_head_kernel_shared_stream(L, case):
+    """The shared stream against each member streaming the whole panel, and
+    against members that never wait for each other (every half that is late
+    scored by the member needing it): the same index sets and outputs, bit
+    for bit, launch after launch on one workspace; oracle parity."""
+    kw = dict(SHARED_CASES[case])
+    wl = _small(**kw)
+    H.log(f"shared stream {case}: {W.describe(wl)}")
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    assert L.decode_plan(dev["desc"], wl.d, wl.k, wl.append)
+    ws = L.empty_workspace(dev["desc"], wl.d, wl.k)
+
+    def run(flags):
+        desc = dev["desc"].with_flags(flags)
+        idx = torch.full((wl.B, wl.Hq, wl.k), -7, dtype=torch.int32, device="cuda")
+        if wl.append:
+            out = L.decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["kcache"], dev["v"],
+                                  dev["P"], wl.d, wl.k, desc, idx_out=idx, workspace=ws)
+        else:
+            out = L.decode(dev["q"], dev["kcache"], dev["v"], dev["P"], wl.d, wl.k, desc,
+                           idx_out=idx, workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), idx.cpu().numpy()
+
+    ref_out, ref_idx = run(L.FLAG_NO_SHARED_STREAM)
+    for flags in (0, 0, L.FLAG_SHARED_NO_WAIT, 0, L.FLAG_SHARED_NO_WAIT):
+        out, idx = run(flags)
+        assert np.array_equal(idx, ref_idx), f"flags {flags}: index sets differ"
+        assert np.array_equal(out.view(np.uint32), ref_out.view(np.uint32)), \
+            f"flags {flags}: outputs differ"
+    H.log(f"  {H.full_parity(wl, x, out.astype(np.float64), idx)}")
+
+
+@pytest.mark.parametrize("fill", ["random", "ones"])
+def test_head_kernel_shared_stream_dirty_workspace(L, fill):
+    """The hand-over flags need no initialisation: a workspace full of
+    garbage (or of 0xff bytes) gives the clean workspace's results, bit for
+    bit, from the first launch on."""
+    wl = _small("bf16", B=2, Hq=8, Hkv=8, S=12000, k=1500)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    out_c, idx_c = _decode_with(L, wl, dev, 0, L.empty_workspace(dev["desc"], wl.d, wl.k))
+    n = L.workspace_bytes(dev["desc"], wl.d, wl.k)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    ws = (torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=g)
+          if fill == "random" else torch.full((n,), 255, dtype=torch.uint8, device="cuda"))
+    for _ in range(2):
+        out, idx = _decode_with(L, wl, dev, 0, ws)
+        assert np.array_equal(idx, idx_c) and np.array_equal(out, out_c)
+    H.log(f"  shared stream, dirty workspace ({fill}): {H.full_parity(wl, x, out, idx)}")
+
+
 @pytest.mark.parametrize("fill", ["random", "ones"])
 def test_helpers_with_dirty_workspace(L, fill):
     """The pair flags need no initialisation: a workspace full of garbage (or
