@@ -23,6 +23,7 @@
 #pragma once
 
 #include "loki_internal.h"
+#include "select_core.h"
 
 namespace loki {
 
@@ -50,9 +51,13 @@ struct AttendSmem {
   float accs[AttendGeom<DT, D, NT>::NG][AttendGeom<DT, D, NT>::DL];
 };
 
+__device__ __forceinline__ float low_logit(float v) { return v; }
+__device__ __forceinline__ float low_logit(unsigned key) { return key_score(key); }
+
 // All NT threads call this together.  qrow: the query in the rotated basis
 // (fp32, global or LDS); sidx[0..nr): token indices in LDS, -1 = skip;
-// slow[0..nr): low-dim partial logits in LDS (split variant only, unscaled);
+// slow[0..nr): low-dim partial logits in LDS (split variant only, unscaled),
+// as floats or as their order keys (select_keys);
 // head: flattened (b, kv) of the caches.  On return thread tid < D holds the
 // merged (M, L, A) with A the unnormalised output coordinate tid, in the log2
 // domain: out[tid] = A / L.
@@ -60,9 +65,9 @@ struct AttendSmem {
 // loads; else (several query heads read the same rows) default-policy loads,
 // which keep the rows in L2 for the other heads.
 template <int DT, int D, int NT, bool SPLIT, int RB = kRowsPerBatch, bool LOW = false,
-          bool STREAM = true>
+          bool STREAM = true, typename Low = float>
 __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2,
-                                             const int* sidx, const float* slow, int nr,
+                                             const int* sidx, const Low* slow, int nr,
                                              const void* kcache, const void* vcache,
                                              size_t head, const Shape& sh,
                                              AttendSmem<DT, D, NT>& sm, float& M_out,
@@ -125,7 +130,7 @@ __device__ __forceinline__ void block_attend(const float* qrow, float scale_log2
       a = group_sum<LPR>(a);
       const int r = rbase + q * NG;
       const bool ok = r < nr && sidx[r] >= 0;
-      if (SPLIT && ok) a = fmaf(slow[r], scale_log2, a);
+      if (SPLIT && ok) a = fmaf(low_logit(slow[r]), scale_log2, a);
       z[q] = ok ? a : -INFINITY;
       mb = fmaxf(mb, z[q]);
     }

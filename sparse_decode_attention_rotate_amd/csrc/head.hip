@@ -130,7 +130,9 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   const int S = sh.S, k = p.k;
   const int Ss = APPEND ? S - 1 : S;  // tokens read from the panel
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* sc = reinterpret_cast<float*>(reuse);  // [S] scores (phase 1)
+  // [S] the scores as order keys (phase 1; -0 as +0): the selection loads
+  // them as they are
+  unsigned* sk = reinterpret_cast<unsigned*>(reuse);
 
   // ---- the query head of this workgroup
   int bh;  // b * Hq + h
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
         for (int e = 0; e < E; e++) a = fmaf(qs[cl * E + e], kn[cl * E + e], a);
         a = group_sum<LPT>(a);
         if (lane == 0) {
-          sc[S - 1] = a;
+          sk[S - 1] = order_key_nz(a + 0.f);
           lo = fminf(lo, a);
           hi = fmaxf(hi, a);
         }
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
         sum += r;
         sq = fmaf(r, r, sq);
       }
-      sc[t] = r;
+      sk[t] = order_key_nz(r + 0.f);  // + 0 turns -0 into +0
       if (hist) atomicAdd(&ssm.hist[lin_bin(r, blo, bscale)], 1u);
     };
     auto consume = [&](const u32x4 (&x)[NB], int pass0, bool hist, bool first) {
@@ -389,9 +391,9 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       }
       bscale = bin_scale(blo, bhi);
       for (int t = t_lo + tid; t < min(t_hi, t_lo + NB * TPP); t += NT)
-        atomicAdd(&ssm.hist[lin_bin(sc[t], blo, bscale)], 1u);
+        atomicAdd(&ssm.hist[lin_bin(key_score(sk[t]), blo, bscale)], 1u);
       if (APPEND && tid == 0)  // the new token (never streamed)
-        atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
+        atomicAdd(&ssm.hist[lin_bin(key_score(sk[S - 1]), blo, bscale)], 1u);
     }
     // every batch is issued, also past the end (those loads are out of range:
     // zeros, no memory access), so that the loads in flight are the same on
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       // they saved (measured)
       LOKI_STAMP(g_stamps_head, 6);
       __syncthreads();  // this half's scores are in LDS
-      for (int t = t_lo + tid; t < t_hi; t += NT) st_coherent(xrow + t, sc[t]);
+      for (int t = t_lo + tid; t < t_hi; t += NT) st_coherent(xrow + t, __uint_as_float(sk[t]));
       wait_stores();
       __syncthreads();  // every store of this half is complete
       unsigned long long* xf = p.xflag + (size_t)pair * 4;
@@ -452,9 +454,8 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
             for (int e = 0; e < 4; e++) {
               const int t = 4 * (q0 + q * NT) + e - sft;
               if (t >= u_lo && t < u_hi) {
-                const float v = __uint_as_float(r[q][e]);
-                sc[t] = v;
-                atomicAdd(&ssm.hist[lin_bin(v, blo, bscale)], 1u);
+                sk[t] = r[q][e];
+                atomicAdd(&ssm.hist[lin_bin(key_score(r[q][e]), blo, bscale)], 1u);
               }
             }
           }
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
           for (int e = 0; e < E; e++) a = fmaf(qv[e], f[e], a);
           a = group_sum<LPT>(a);
           if (c == 0 && t < u_hi) {
-            sc[t] = a;
+            sk[t] = order_key_nz(a + 0.f);
             atomicAdd(&ssm.hist[lin_bin(a, blo, bscale)], 1u);
           }
         }
@@ -494,17 +495,15 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   __syncthreads();  // every score is in LDS
   LOKI_STAMP(g_stamps_head, 2);
 
-  // ---- 2. top-k: the scores as order keys in registers, then the LDS reused
-  int* sidx = reinterpret_cast<int*>(reuse);                   // [k]
-  float* slow = reinterpret_cast<float*>(reuse + L::slow(k));  // [k]
+  // ---- 2. top-k: the order keys in registers, then the LDS reused
+  int* sidx = reinterpret_cast<int*>(reuse);                         // [k]
+  unsigned* skey = reinterpret_cast<unsigned*>(reuse + L::slow(k));  // [k] their keys
   auto whist = reinterpret_cast<unsigned (*)[256]>(reuse + L::whist(k));
   auto& asm_ = *reinterpret_cast<AttendSmem<DT, D, NT>*>(reuse + L::att(k));
   {
-    // padding elements read as the all-ones NaN, order key 0 (select_keys)
-    auto ld = [&](int i) -> float { return i < S ? sc[i] : __uint_as_float(0xffffffffu); };
-    RowView<NT, KREG, decltype(ld)> row(ld, S);
-    __syncthreads();  // every key is in registers: the scores' LDS is free
-    select_keys<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, whist);
+    KeyRow<NT, KREG> row(sk, S);  // elements past the row: key 0 (select_keys)
+    __syncthreads();              // every key is in registers: the row's LDS is free
+    select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, whist);
   }
   LOKI_STAMP(g_stamps_head, 3);
   if constexpr (APPEND) {
@@ -524,7 +523,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   const int nr = paired ? (helper ? k - p.k0 : p.k0) : k;
   float M, Lsum, A;
   block_attend<DT, D, NT, true, kHeadRowsPerBatch, false, true>(
-      qs, p.scale_log2, sidx + r0, slow + r0, nr, p.kcache, p.vcache, head, sh, asm_, M, Lsum, A);
+      qs, p.scale_log2, sidx + r0, skey + r0, nr, p.kcache, p.vcache, head, sh, asm_, M, Lsum, A);
   if (paired) {
     // owner: rows [0, k0); helper: rows [k0, k).  Partials (M, L, A[D]) of
     // pair j: owner's at help_part[2j], helper's at help_part[2j+1].

@@ -47,6 +47,13 @@ __host__ __device__ __forceinline__ unsigned order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// order_key for a score that is not -0 (the caller adds +0, which turns -0
+// into +0 and leaves every other value as it is): three instructions.
+__host__ __device__ __forceinline__ unsigned order_key_nz(float s) {
+  const unsigned u = __builtin_bit_cast(unsigned, s);
+  return u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
+}
+
 // Inverse of order_key (a -0 score comes back as +0).
 __host__ __device__ __forceinline__ float key_score(unsigned key) {
   return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
@@ -156,6 +163,37 @@ struct RowView {
   }
 };
 
+// A thread's share of a row of S order keys held in LDS (element j of the
+// thread: index wave*KREG*64 + j*64 + lane, as RowView), kept in registers;
+// elements past the row get key 0.  keys[i] is read for i < S only.
+template <int NT, int KREG>
+struct KeyRow {
+  static_assert(KREG > 0, "keys in registers");
+  int S, per_wave, base;
+  unsigned kv[KREG];
+
+  __device__ __forceinline__ KeyRow(const unsigned* keys, int S_) : S(S_) {
+    per_wave = KREG * 64;
+    base = (threadIdx.x >> 6) * per_wave + (threadIdx.x & 63);
+    if (S >= NT * KREG) {  // a full row: no element to check
+#pragma unroll
+      for (int j = 0; j < KREG; j++) kv[j] = keys[base + j * 64];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KREG; j++) {
+        const int i = base + j * 64;
+        kv[j] = i < S ? keys[i] : 0u;
+      }
+    }
+  }
+
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) {
+#pragma unroll
+    for (int j = 0; j < KREG; j++) f(base + j * 64, kv[j]);
+  }
+};
+
 // Step 1b: descending scan over the histogram; sets sm.sel_bin (the bin b*
 // holding the k-th largest score), sm.sel_gt (members of higher bins) and
 // sm.sel_eq (members of b*).  All NT threads; ends with a barrier.
@@ -198,8 +236,8 @@ __device__ __forceinline__ void select_scan(SM& sm, int k) {
 // with a barrier.
 // PADDED: member() is false for every padding element (index >= S), so the
 // index is not checked.
-template <int NT, int KREG, bool PADDED = false, typename Load, typename SM, typename Member>
-__device__ __forceinline__ void radix_threshold_of(RowView<NT, KREG, Load>& row, Member&& member,
+template <int NT, int KREG, bool PADDED = false, typename Row, typename SM, typename Member>
+__device__ __forceinline__ void radix_threshold_of(Row& row, Member&& member,
                                                    int rem, SM& sm, unsigned (*whist)[256]) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -496,31 +534,34 @@ __device__ __forceinline__ unsigned long long first_key_of_bin(unsigned long lon
 //    linear sub-bins (one pass over the interval's keys and a scan) and the
 //    interval narrowed to the sub-bin holding the k-th score; radix passes
 //    over the interval's keys resolve a group still crowded after that;
-//  * one pass counts, per wave, the keys above the interval and marks the
-//    interval's keys (a bit per key, registers only); each wave copies its
-//    marked candidates to LDS at slots it reserves at once; the candidates
-//    are ranked by (key descending, index ascending) and the rem first are
-//    taken; (T, I) is the last taken;
+//  * one pass counts, per wave, the keys above the interval (a ballot and a
+//    scalar count per key slot) and copies the interval's keys, the
+//    candidates, to LDS (rare: a slot holding some reserves consecutive
+//    places at once); the candidates are ranked by (key descending, index
+//    ascending) and the rem first are taken; (T, I) is the last taken;
 //  * one pass writes the taken elements: element i with key > T, or
 //    key == T and i <= I.  Key slot j of a wave holds 64 consecutive
 //    indices, so one ballot per slot places them after the counts of the
 //    waves and ballots before: the output is in ascending index order.
-// Padding elements (index >= S) must have key 0 (load_score gives them the
-// all-ones NaN) and no score may have those bits: key 0 is then never taken
-// and no pass checks the index.  sm.hist holds the histogram under
-// (lo, scale) and sm.n_cand is 0; whist: the radix passes' per-wave
-// histograms.  Writes k entries of out_idx / out_val (the taken indices, in
-// ascending order, and their scores, -0 as +0) and sm.thr_key / sm.thr_idx =
-// (T, I).  All NT threads; the caller needs a barrier before reading the
-// output.
-template <int NT, int KREG, typename Load, typename SM>
-__device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k, int32_t* out_idx,
-                                            float* out_val, SM& sm, float lo, float scale,
+// The passes are bound by vector instructions per key (a wave64 instruction
+// takes its SIMD four cycles), hence the scalar counts.
+// Padding elements (index >= S) must have key 0 (RowView's load_score gives
+// them the all-ones NaN, KeyRow key 0) and no score may have those bits: key
+// 0 is then never taken and no pass checks the index.  sm.hist holds the
+// histogram under (lo, scale) and sm.n_cand is 0; whist: the radix passes'
+// per-wave histograms.  Writes k entries of out_idx / out_key (the taken
+// indices, in ascending order, and their order keys) and sm.thr_key /
+// sm.thr_idx = (T, I).  All NT threads; the caller needs a barrier before
+// reading the output.
+template <int NT, int KREG, typename Row, typename SM>
+__device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, unsigned* out_key,
+                                            SM& sm, float lo, float scale,
                                             unsigned (*whist)[256]) {
   constexpr int NW = NT / 64;
   static_assert(NW >= 2, "two waves search the interval's ends");
   static_assert(KREG > 0 && KREG <= 32, "keys in registers, a bit per key of a thread");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index in a scalar register: offsets and counts below stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   select_scan<NT>(sm, k);  // ends with a barrier
   const int bstar = sm.sel_bin;
@@ -572,38 +613,29 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
 
   // ---- the last taken element (T, I) and each wave's number of taken ones
   if (nb <= kFewCandidates) {
-    unsigned gt = 0u, cmask = 0u;
     const unsigned span = khi1 - klo;  // key - klo <= span: klo <= key <= khi1
+    int gt = 0;                        // this wave's keys above the interval
 #pragma unroll
     for (int j = 0; j < KREG; j++) {
       const unsigned key = row.kv[j];
-      gt += key > khi1 ? 1u : 0u;
-      cmask |= (key - klo <= span) ? (1u << j) : 0u;
-    }
-    if (__ballot(cmask != 0u) != 0ull) {  // rare: this wave holds members of the group
-      // the wave's candidates take consecutive slots: one reservation, then
-      // a ballot per key slot (at most kFewCandidates in all: the group's
-      // members are exactly the nb elements its bin counted)
-      const int nc = (int)wave_sum((float)__popc(cmask));  // exact: at most 64 * KREG
-      int slot = 0;
-      if (lane == 0) slot = atomicAdd(&sm.n_cand, nc);
-      slot = __shfl(slot, 0, 64);
-#pragma unroll
-      for (int j = 0; j < KREG; j++) {
-        const bool c = (cmask >> j) & 1u;
-        const unsigned long long m = __ballot(c);
-        if (m != 0ull) {
-          if (c) {
-            const int at = slot + lane_rank(m);
-            sm.cand_key[at] = row.kv[j];
-            sm.cand_idx[at] = row.base + j * 64;
-          }
-          slot += __popcll(m);
+      gt += __popcll(__ballot(key > khi1));
+      const bool c = key - klo <= span;
+      const unsigned long long m = __ballot(c);
+      if (m != 0ull) {
+        // rare: the slot's candidates take consecutive places (at most
+        // kFewCandidates in all: the group's members are exactly the nb
+        // elements its bin counted)
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&sm.n_cand, __popcll(m));
+        slot = __builtin_amdgcn_readfirstlane(slot);
+        if (c) {
+          const int at = slot + lane_rank(m);
+          sm.cand_key[at] = key;
+          sm.cand_idx[at] = row.base + j * 64;
         }
       }
     }
-    gt = (unsigned)wave_sum((float)gt);  // exact: counts below 2^24
-    if (lane == 0) sm.wcnt[wave] = (int)gt;
+    if (lane == 0) sm.wcnt[wave] = gt;
     __syncthreads();
     // rank of candidate c = members ordered before it by (key descending,
     // index ascending): one ballot over the candidates on the lanes; the
@@ -632,14 +664,13 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
         row, [&](unsigned key) { return key >= klo && key <= khi1; }, rem, sm, whist);
     const unsigned T = sm.thr_key;
     const int I = sm.thr_idx;
-    unsigned cnt = 0u;
+    int cnt = 0;
 #pragma unroll
     for (int j = 0; j < KREG; j++) {
       const unsigned key = row.kv[j];
-      cnt += (key > T || (key == T && row.base + j * 64 <= I)) ? 1u : 0u;
+      cnt += __popcll(__ballot(key > T || (key == T && row.base + j * 64 <= I)));
     }
-    cnt = (unsigned)wave_sum((float)cnt);
-    if (lane == 0) sm.wcnt[wave] = (int)cnt;
+    if (lane == 0) sm.wcnt[wave] = cnt;
     __syncthreads();
   }
 
@@ -649,16 +680,19 @@ __device__ __forceinline__ void select_keys(RowView<NT, KREG, Load>& row, int k,
   const int I = sm.thr_idx;
   int out = 0;
   for (int w = 0; w < wave; w++) out += sm.wcnt[w];
+  const int ib = I - wave * row.per_wave;  // element i <= I: lane <= ib - 64 j
 #pragma unroll
   for (int j = 0; j < KREG; j++) {
     const unsigned key = row.kv[j];
-    const int i = row.base + j * 64;
-    const bool take = key > T || (key == T && i <= I);
-    const unsigned long long m = __ballot(take);
-    if (take) {
+    // the ballot from the three comparisons' lane masks (scalar and / or),
+    // the branch from the same comparisons
+    const bool gt = key > T, eq = key == T, le = lane <= ib - j * 64;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(gt) |
+                                 (__builtin_amdgcn_ballot_w64(eq) & __builtin_amdgcn_ballot_w64(le));
+    if (gt || (eq && le)) {
       const int at = out + lane_rank(m);
-      out_idx[at] = i;
-      out_val[at] = key_score(key);
+      out_idx[at] = row.base + j * 64;
+      out_key[at] = key;
     }
     out += __popcll(m);
   }

@@ -8,7 +8,8 @@ far from and much wider or narrower than the data:
   * every bin lies in [0, 2047];
   * bins never decrease as the order key grows (the exact selection relies on
     every score of a higher bin ranking above every score of a lower one);
-  * order_key / key_score round-trip every value (-0 comes back as +0).
+  * order_key / key_score round-trip every value (-0 comes back as +0);
+  * order_key_nz of a value plus +0 is its order_key (NaN aside).
 """
 import os
 import subprocess
@@ -52,6 +53,15 @@ int main() {
     const float back = key_score(order_key(v));
     const unsigned want = bits(v) == 0x80000000u ? 0u : bits(v);
     if (bits(back) != want) { printf("FAIL roundtrip %08x -> %08x\n", bits(v), bits(back)); return 1; }
+  }
+
+  // order_key_nz after adding +0 (-0 becomes +0) equals order_key for every
+  // value but NaN (whose payload the addition may change)
+  volatile float zero = 0.f;
+  for (float v : s) {
+    if (v != v) continue;
+    const unsigned a = order_key_nz(v + zero), b = order_key(v);
+    if (a != b) { printf("FAIL order_key_nz %08x: %08x != %08x\n", bits(v), a, b); return 1; }
   }
 
   struct R { float lo, scale; };
