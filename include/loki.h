@@ -133,6 +133,12 @@ typedef struct {
    its partner is not resident within 20 us).  Same results, bit for bit. */
 #define LOKI_FLAG_SHARED_NO_WAIT 8u
 
+/* loki_desc.flags: take the one-launch kernel with one query head per
+   workgroup (plan 2 of loki_decode_plan) also where the one with one
+   workgroup per (b, kv) applies.  Same index sets; outputs equal up to fp32
+   summation order. */
+#define LOKI_FLAG_PER_HEAD_KERNEL 16u
+
 /* Human-readable name of a status code; never NULL. */
 const char* loki_strerror(int status);
 

@@ -30,6 +30,7 @@ FLAG_SEPARATE_KERNELS = 1
 FLAG_NO_HELPERS = 2
 FLAG_NO_SHARED_STREAM = 4
 FLAG_SHARED_NO_WAIT = 8
+FLAG_PER_HEAD_KERNEL = 16
 NOALLOC_SCRATCH_BYTES = 64 << 20  # LOKI_NOALLOC_SCRATCH_BYTES of include/loki.h
 DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}

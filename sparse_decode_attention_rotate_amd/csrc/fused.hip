@@ -15,7 +15,10 @@
 //     their min / max folded on the way;
 //  0'. the loads for the remaining D-dp coordinates of the rotation are issued
 //     and stay in flight through the top-k;
-//  2. block_select (select_core.h) picks each head's top k from LDS;
+//  2. top-k from LDS: a single head's scores are stored as order keys while
+//     streaming (its histogram built as they come) and select_keys
+//     (select_core.h) takes them from registers; several heads' scores go
+//     through block_select one head at a time;
 //  3. block_attend (attend_core.h) gathers the selected key tails and value
 //     rows and writes the output rows.
 // A decode step becomes one kernel: no launch gaps, no ramp-up/drain between
@@ -84,6 +87,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   const int S = sh.S, k = p.k;
   const int Ss = APPEND ? S - 1 : S;  // tokens read from the panel
   float* sc = reinterpret_cast<float*>(dyn);             // [G][S]
+  // single head: the scores as order keys (-0 as +0), which the selection
+  // loads as they are
+  unsigned* sk = reinterpret_cast<unsigned*>(dyn);
   int* sidx = reinterpret_cast<int*>(sc + G * S);        // [G][k]
   float* slow = reinterpret_cast<float*>(sidx + G * k);  // [G][k]
 
@@ -235,7 +241,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
         for (int e = 0; e < E; e++) a = fmaf(qs[h][cl * E + e], kn[cl * E + e], a);
         a = group_sum<LPT>(a);
         if (lane < G * LPT && cl == 0) {
-          sc[h * S + S - 1] = a;
+          if constexpr (G == 1)
+            sk[S - 1] = order_key_nz(a + 0.f);
+          else
+            sc[h * S + S - 1] = a;
 #pragma unroll
           for (int hh = 0; hh < G; hh++)
             if (hh == h) {
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
           if (t < Ss) {
             lo[0] = fminf(lo[0], r);
             hi[0] = fmaxf(hi[0], r);
-            sc[t] = r;
+            sk[t] = order_key_nz(r + 0.f);  // + 0 turns -0 into +0
             if (hist) atomicAdd(&ssm.hist[lin_bin(r, blo, bscale)], 1u);
           }
         }
@@ -292,8 +301,12 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
             lo[h] = fminf(lo[h], a);
             hi[h] = fmaxf(hi[h], a);
             if (c == (h % LPT)) {
-              sc[h * S + t] = a;
-              if (G == 1 && hist) atomicAdd(&ssm.hist[lin_bin(a, blo, bscale)], 1u);
+              if constexpr (G == 1) {
+                sk[t] = order_key_nz(a + 0.f);
+                if (hist) atomicAdd(&ssm.hist[lin_bin(a, blo, bscale)], 1u);
+              } else {
+                sc[h * S + t] = a;
+              }
             }
           }
         }
@@ -317,9 +330,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       }
       bscale = bin_scale(blo, bhi);
       for (int t = tid; t < min(S, NB * TPP); t += NT)
-        atomicAdd(&ssm.hist[lin_bin(sc[t], blo, bscale)], 1u);
+        atomicAdd(&ssm.hist[lin_bin(key_score(sk[t]), blo, bscale)], 1u);
       if (APPEND && tid == 0 && S - 1 >= NB * TPP)  // the new token, past the first batch
-        atomicAdd(&ssm.hist[lin_bin(sc[S - 1], blo, bscale)], 1u);
+        atomicAdd(&ssm.hist[lin_bin(key_score(sk[S - 1]), blo, bscale)], 1u);
     }
     // every batch is issued, also past the end (those loads are out of range:
     // zeros, no memory access), so that the loads in flight are the same on
@@ -372,14 +385,11 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   if constexpr (APPEND) vraw = static_cast<const Raw*>(p.v_new)[head * D + min(tid, D - 1)];
   __syncthreads();
 
-  // ---- 2. top-k of each head's scores, from LDS
-  // Single head (the per-wave lists hold every row above the threshold bin):
-  // the selected rows come in two index-ordered parts and the attention
-  // starts as soon as they are known; the partial rotation sums go to LDS
-  // inside the selection's barriers.
-  constexpr bool kStreamRows = G == 1;
-  const bool stream_rows =
-      kStreamRows && (KREG * 64 <= kRowListCap<NT> || k - 1 <= kRowListCap<NT>);
+  // ---- 2. top-k of each head's scores, from LDS.  Single head: the order
+  // keys go to registers and select_keys (select_core.h) writes the selected
+  // tokens in ascending order with their keys, which the attention reads as
+  // the partial logits.  Several heads: block_select per head.
+  unsigned* skey = reinterpret_cast<unsigned*>(slow);  // [k] (single head)
   auto rotate_rest = [&]() {  // qpart[w][h][DP:D] from the P loads in flight
     float a[GR][4];
 #pragma unroll
@@ -426,18 +436,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
       wait_stores();
     }
   };
-  if (stream_rows) {
-    auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
-    RowView<NT, KREG, decltype(load_score)> row(load_score, S);
-    select_rows<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, rotate_rest);
-    reduce_rest();
-    __syncthreads();
-  } else {
-    if (G == 1) {
-      auto load_score = [&](int i) -> float { return sc[i < S ? i : 0]; };
-      RowView<NT, KREG, decltype(load_score)> row(load_score, S);
-      select_from_histogram<NT, KREG>(row, k, sidx, slow, ssm, blo, bscale, ssm.whist);
-      __syncthreads();
+  {
+    if constexpr (G == 1) {
+      KeyRow<NT, KREG> row(sk, S);  // elements past the row: key 0 (select_keys)
+      select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, ssm.whist);
     } else {
       for (int h = 0; h < G; h++) {
         float l0 = rng[0][0][h], h0 = rng[1][0][h];
@@ -465,21 +467,28 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   // ---- 3. exact attention over the selected tokens of each head
   // (the index sets, when asked for, are written after it: off its critical path)
   auto write_idx = [&]() {
-    if (p.idx_out && !helper) {
-      if (stream_rows)
-        write_rows_in_index_order(sidx, ssm.sel_gt, k, p.idx_out + q0 * k, NT);
-      else
-        for (int e = tid; e < G * k; e += NT) p.idx_out[q0 * k + e] = sidx[e];
-    }
+    if (p.idx_out && !helper)
+      for (int e = tid; e < G * k; e += NT) p.idx_out[q0 * k + e] = sidx[e];
+  };
+  // rows [r0, r0 + nr) of head h's selected list (single head: the partial
+  // logits as order keys, rows read once; several heads: as floats, rows
+  // kept in L2 for the group's other heads)
+  auto attend = [&](int h, int r0, int nr, float& M, float& L, float& A) {
+    if constexpr (G == 1)
+      block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, true>(
+          qs[0], p.scale_log2, sidx + r0, skey + r0, nr, p.kcache, p.vcache, head, sh, asm_, M,
+          L, A);
+    else
+      block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, false>(
+          qs[h], p.scale_log2, sidx + h * k + r0, slow + h * k + r0, nr, p.kcache, p.vcache,
+          head, sh, asm_, M, L, A);
   };
   if (paired) {
     // owner: rows [0, k0); helper: rows [k0, k).  Partials (M, L, A[D]) of
     // pair j: owner's at help_part[2j], helper's at help_part[2j+1].
     const int r0 = helper ? p.k0 : 0, nr = helper ? k - p.k0 : p.k0;
     float M, L, A;
-    block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, G == 1>(qs[0], p.scale_log2, sidx + r0, slow + r0,
-                                                      nr, p.kcache, p.vcache, head, sh, asm_, M,
-                                                      L, A);
+    attend(0, r0, nr, M, L, A);
     float* mine = p.help_part + ((size_t)pair * 2 + (helper ? 1 : 0)) * (D + 2);
     const float* other = p.help_part + ((size_t)pair * 2 + (helper ? 0 : 1)) * (D + 2);
     if (tid < D) st_coherent(mine + 2 + tid, A);
@@ -514,8 +523,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   }
   for (int h = 0; h < G; h++) {
     float M, L, A;
-    block_attend<DT, D, NT, true, kFusedRowsPerBatch, false, G == 1>(qs[h], p.scale_log2, sidx + h * k, slow + h * k, k,
-                                  p.kcache, p.vcache, head, sh, asm_, M, L, A);
+    attend(h, 0, k, M, L, A);
     if (tid < D) store_out(p.out, (q0 + h) * D + tid, A / L, sh.odt);
     __syncthreads();  // asm_ is reused by the next head
   }

@@ -564,18 +564,24 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
 // compute unit) while a row's scores fit half of the LDS, else 1024.
 int head_threads(int S) { return S <= 512 * 32 && S * 4 <= 64 * 1024 ? 512 : 1024; }
 
-template <int DT, int D, int LPT, int NT, bool APPEND>
+template <int DT, int D, int LPT, int NT, int KREG, bool APPEND>
 hipError_t launch_v(const HeadParams& p, hipStream_t st) {
   const size_t dyn = HeadLds<DT, D, NT, APPEND ? 2 : 1>::bytes(p.sh.S, p.k);
   const dim3 grid((unsigned)(p.n_slots + p.n_help));
-  head_kernel<DT, D, LPT, NT, 32, APPEND><<<grid, NT, dyn, st>>>(p);
+  head_kernel<DT, D, LPT, NT, KREG, APPEND><<<grid, NT, dyn, st>>>(p);
   return hipGetLastError();
 }
 
+// Order keys per thread in the selection: the fewest that hold the row, so
+// that every wave of a short row holds keys (a wave owns KREG * 64
+// consecutive tokens).
 template <int DT, int D, int LPT, bool APPEND>
 hipError_t launch_a(const HeadParams& p, hipStream_t st) {
-  return head_threads(p.sh.S) == 512 ? launch_v<DT, D, LPT, 512, APPEND>(p, st)
-                                     : launch_v<DT, D, LPT, 1024, APPEND>(p, st);
+  const int S = p.sh.S;
+  if (head_threads(S) == 1024) return launch_v<DT, D, LPT, 1024, 32, APPEND>(p, st);
+  if (S <= 512 * 8) return launch_v<DT, D, LPT, 512, 8, APPEND>(p, st);
+  if (S <= 512 * 16) return launch_v<DT, D, LPT, 512, 16, APPEND>(p, st);
+  return launch_v<DT, D, LPT, 512, 32, APPEND>(p, st);
 }
 
 template <int DT, int D, int LPT>

@@ -227,7 +227,8 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* kcach
 
   // the one-launch kernel keeps the scores on chip: a call that asks for
   // them takes the separate launches
-  if (!scores_out && !(desc->flags & LOKI_FLAG_SEPARATE_KERNELS) && fused_supported(sh, d, k)) {
+  if (!scores_out && !(desc->flags & (LOKI_FLAG_SEPARATE_KERNELS | LOKI_FLAG_PER_HEAD_KERNEL)) &&
+      fused_supported(sh, d, k)) {
     FusedParams fp{};
     fp.q = q;
     fp.k_new = append ? k_new : nullptr;
@@ -456,7 +457,9 @@ int loki_decode_plan(const loki_desc* desc, int d, int k, int append, int* one_l
   (void)append;  // the one-launch kernel appends too
   *one_launch = 0;
   if (!(desc->flags & LOKI_FLAG_SEPARATE_KERNELS))
-    *one_launch = fused_supported(sh, d, k) ? 1 : (head_supported(sh, d, k) ? 2 : 0);
+    *one_launch = fused_supported(sh, d, k) && !(desc->flags & LOKI_FLAG_PER_HEAD_KERNEL)
+                      ? 1
+                      : (head_supported(sh, d, k) ? 2 : 0);
   return LOKI_OK;
 }
 

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
 
 // Tokens per tile of the panel kernel with LPT lanes per token: up to 4096
 // (256 KB of an fp16 panel), smaller when that leaves fewer than two
-// workgroups per compute unit (eight when a tile also writes the scores of
+// workgroups per compute unit (four when a tile also writes the scores of
 // several heads); multiples of two batches; staged tiles hold all g heads'
 // scores of the tile in LDS.
 int tile_tokens(const Shape& sh, int lpt) {
