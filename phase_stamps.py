@@ -30,7 +30,7 @@ import workloads as W
 
 PHASES = {1: ("fused", ["rotation", "scores", "selection", "attention"]),
           2: ("head", ["rotation", "scores", "selection", "append wait", "attention"])}
-SLOTS = 8  # kStampSlots of csrc/phase_stamps.h
+SLOTS = 16  # kStampSlots of csrc/phase_stamps.h (the last holds HW_ID)
 MAX_WG = 8192
 
 
@@ -129,11 +129,13 @@ def main():
     for tt in np.arange(0, ts[:, -1].max() + 5, 5.0):
         ph = [int(((ts[:, i] <= tt) & (ts[:, i + 1] > tt)).sum()) for i in range(len(names))]
         lines.append(f"   t={tt:6.1f} " + " ".join(f"{nm}:{c:4d}" for nm, c in zip(names, ph)))
-    extra = s[used][:, nb:7]
+    extra = s[used][:, nb:SLOTS - 1]
     for j in range(extra.shape[1]):
         if (extra[:, j] > 0).all():
             e = (extra[:, j] - s[used][:, 0].min()) / 100.0
             lines.append(f"  slot {nb + j}: p50 {np.median(e):7.2f} max {e.max():7.2f}")
+        elif (extra[:, j] > 0).any():
+            lines.append(f"  slot {nb + j}: written by {(extra[:, j] > 0).sum()} workgroups")
     text = "\n".join(lines)
     print(text)
     if args.out:

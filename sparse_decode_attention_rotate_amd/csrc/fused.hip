@@ -53,8 +53,11 @@ constexpr int kFusedBatch = 8;            // 16-byte panel loads per lane per ba
 constexpr size_t kFusedDynBytes = 36 * 1024;
 constexpr int kFusedRowsPerBatch = 4;  // gather rows per lane group per batch
 
-// phase stamps (profiling builds): 0 start, 1 rotation done, 2 scores in
-// LDS, 3 selection (and the rest of the rotation) done, 4 end
+// phase stamps (profiling builds): 0 start, 1 rotation done, 2 wave 0's
+// scores in LDS, 3 selection (and the rest of the rotation) done, 4 end,
+// 5 every wave's scores in LDS; inside the single-head selection (wave 0):
+// 6 threshold group known, 7 last taken element known, 8 taken elements
+// written
 LOKI_STAMP_ARRAY(g_stamps_fused);
 
 template <int DT, int D, int LPT, int G, int NT, bool APPEND>
@@ -384,6 +387,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   Raw vraw = 0;
   if constexpr (APPEND) vraw = static_cast<const Raw*>(p.v_new)[head * D + min(tid, D - 1)];
   __syncthreads();
+  LOKI_STAMP(g_stamps_fused, 5);
 
   // ---- 2. top-k of each head's scores, from LDS.  Single head: the order
   // keys go to registers and select_keys (select_core.h) writes the selected
@@ -439,7 +443,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   {
     if constexpr (G == 1) {
       KeyRow<NT, KREG> row(sk, S);  // elements past the row: key 0 (select_keys)
-      select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, ssm.whist);
+      select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, ssm.whist,
+                            [&](int i) { LOKI_STAMP(g_stamps_fused, 6 + i); });
     } else {
       for (int h = 0; h < G; h++) {
         float l0 = rng[0][0][h], h0 = rng[1][0][h];

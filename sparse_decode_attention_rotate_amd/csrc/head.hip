@@ -96,8 +96,12 @@ __device__ __forceinline__ void pair_share_done(unsigned long long* xf, unsigned
 }
 
 // phase stamps (profiling builds): 0 start, 1 rotation done, 2 scores in
-// LDS, 3 selection done, 4 attention starts, 5 end, 6 own half of the
-// scores done (pairs sharing the stream)
+// LDS, 3 selection done, 4 attention starts, 5 end; pairs sharing the stream:
+// 6 wave 0 through its half of the stream, 7 every wave through it, 8 the
+// half published, 9 the partner's flag seen (or the wait over), 10 the
+// partner's half in LDS, 11 written only when the wait timed out; inside
+// the selection (wave 0): 12 threshold group known, 13 last taken element
+// known, 14 taken elements written
 LOKI_STAMP_ARRAY(g_stamps_head);
 
 template <int DT, int D, int LPT, int NT, int KREG, bool APPEND>
@@ -421,15 +425,19 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
       // they saved (measured)
       LOKI_STAMP(g_stamps_head, 6);
       __syncthreads();  // this half's scores are in LDS
+      LOKI_STAMP(g_stamps_head, 7);
       for (int t = t_lo + tid; t < t_hi; t += NT) st_coherent(xrow + t, __uint_as_float(sk[t]));
       wait_stores();
       __syncthreads();  // every store of this half is complete
+      LOKI_STAMP(g_stamps_head, 8);
       unsigned long long* xf = p.xflag + (size_t)pair * 4;
       if (tid == 0) {
         __hip_atomic_store(xf + member, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         xok = wait_flag(xf + (1 - member), p.tag, p.wait_ticks);
       }
       __syncthreads();
+      LOKI_STAMP(g_stamps_head, 9);
+      if (!xok) LOKI_STAMP(g_stamps_head, 11);  // the partner's half is scored here
       const int u_lo = member ? 0 : half * TPP, u_hi = member ? half * TPP : Ss;
       if (xok) {
         // 16-byte agent-coherent loads (sc1), four in flight per thread, over
@@ -480,6 +488,7 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
           }
         }
       }
+      LOKI_STAMP(g_stamps_head, 10);
       if (tid == 0) pair_share_done(xf, p.tag);
     }
   }
@@ -503,7 +512,8 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   {
     KeyRow<NT, KREG> row(sk, S);  // elements past the row: key 0 (select_keys)
     __syncthreads();              // every key is in registers: the row's LDS is free
-    select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, whist);
+    select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, whist,
+                          [&](int i) { LOKI_STAMP(g_stamps_head, 12 + i); });
   }
   LOKI_STAMP(g_stamps_head, 3);
   if constexpr (APPEND) {

@@ -3,7 +3,7 @@
 // Built with LOKI_PHASE_STAMPS defined (the library libloki_stamps.so, built
 // by `python -m sparse_decode_attention_rotate_amd.build --stamps`), thread 0
 // of each workgroup records the constant 100 MHz clock (s_memrealtime) at the
-// boundaries of its phases into a per-kernel device array, and slot 7 holds
+// boundaries of its phases into a per-kernel device array, and the last slot holds
 // the workgroup's HW_ID register (compute unit, shader engine); the library
 // exports loki_phase_stamps_fused / loki_phase_stamps_head to copy them out.
 // In the product library every stamp compiles to nothing.
@@ -12,7 +12,7 @@
 #include <hip/hip_runtime.h>
 
 namespace loki {
-constexpr int kStampSlots = 8;            // per workgroup: phase boundaries 0..6, HW_ID at 7
+constexpr int kStampSlots = 16;           // per workgroup: phase boundaries 0..14, HW_ID at 15
 constexpr int kStampWorkgroups = 8192;    // workgroups recorded (the first ones of a launch)
 }  // namespace loki
 
@@ -28,7 +28,7 @@ constexpr int kStampWorkgroups = 8192;    // workgroups recorded (the first ones
 #define LOKI_STAMP_HWID(arr)                                                           \
   do {                                                                                 \
     if (threadIdx.x == 0 && blockIdx.x < (unsigned)loki::kStampWorkgroups)             \
-      arr[blockIdx.x * loki::kStampSlots + 7] =                                        \
+      arr[blockIdx.x * loki::kStampSlots + loki::kStampSlots - 1] =                                        \
           (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4);                         \
   } while (0)
 #define LOKI_STAMP_EXPORT(fn, arr)                                                     \

@@ -553,10 +553,13 @@ __device__ __forceinline__ unsigned long long first_key_of_bin(unsigned long lon
 // indices, in ascending order, and their order keys) and sm.thr_key /
 // sm.thr_idx = (T, I).  All NT threads; the caller needs a barrier before
 // reading the output.
-template <int NT, int KREG, typename Row, typename SM>
+// mark(i) is called at three points (profiling builds record a time stamp):
+// 0 the threshold group's keys known, 1 the last taken element known, 2 this
+// wave's taken elements written.
+template <int NT, int KREG, typename Row, typename SM, typename Mark>
 __device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, unsigned* out_key,
                                             SM& sm, float lo, float scale,
-                                            unsigned (*whist)[256]) {
+                                            unsigned (*whist)[256], Mark&& mark) {
   constexpr int NW = NT / 64;
   static_assert(NW >= 2, "two waves search the interval's ends");
   static_assert(KREG > 0 && KREG <= 32, "keys in registers, a bit per key of a thread");
@@ -611,6 +614,7 @@ __device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, u
     khi1 = sm.key_hi1;
   }
 
+  mark(0);
   // ---- the last taken element (T, I) and each wave's number of taken ones
   if (nb <= kFewCandidates) {
     const unsigned span = khi1 - klo;  // key - klo <= span: klo <= key <= khi1
@@ -674,6 +678,7 @@ __device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, u
     __syncthreads();
   }
 
+  mark(1);
   // ---- write the taken elements: key slot j of a wave holds 64 consecutive
   // indices, so a ballot per slot writes them in ascending index order
   const unsigned T = sm.thr_key;
@@ -696,6 +701,14 @@ __device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, u
     }
     out += __popcll(m);
   }
+  mark(2);
+}
+
+template <int NT, int KREG, typename Row, typename SM>
+__device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, unsigned* out_key,
+                                            SM& sm, float lo, float scale,
+                                            unsigned (*whist)[256]) {
+  select_keys<NT, KREG>(row, k, out_idx, out_key, sm, lo, scale, whist, [](int) {});
 }
 
 // Entries of each wave's list in select_rows: the lists fill sm.hist and

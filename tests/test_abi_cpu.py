@@ -51,7 +51,8 @@ def test_header_flags_match_binding(L):
     src = open(HEADER).read()
     flags = dict(re.findall(r"#define\s+LOKI_(FLAG_\w+)\s+(\d+)u", src))
     assert flags == {"FLAG_SEPARATE_KERNELS": "1", "FLAG_NO_HELPERS": "2",
-                     "FLAG_NO_SHARED_STREAM": "4", "FLAG_SHARED_NO_WAIT": "8"}
+                     "FLAG_NO_SHARED_STREAM": "4", "FLAG_SHARED_NO_WAIT": "8",
+                     "FLAG_PER_HEAD_KERNEL": "16"}
     for name, v in flags.items():
         assert getattr(L, name) == int(v)
 

@@ -764,6 +764,29 @@ def test_helpers_match_solo_units(L, dtype, B, nh, S, k):
     H.log(f"  helpers {dtype} B={B} heads={nh}: {res}")
 
 
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,S,k", [("f16", 4, 8, 8, 4096, 1024),
+                                               ("bf16", 2, 8, 4, 2500, 250),
+                                               ("f16", 3, 4, 4, 8000, 700),
+                                               ("f32", 2, 4, 2, 1500, 200)])
+def test_per_head_kernel_flag(L, dtype, B, Hq, Hkv, S, k):
+    """Shapes the one-workgroup-per-(b, kv) kernel takes, run with
+    LOKI_FLAG_PER_HEAD_KERNEL through the one-workgroup-per-head kernel (its
+    8-, 16- and 32-key register variants): plan 2, the default plan's index
+    sets, its outputs up to fp32 summation order, oracle parity."""
+    wl = _small(dtype, B=B, Hq=Hq, Hkv=Hkv, S=S, k=k)
+    x = W.generate(wl)
+    dev = H.upload(wl, x)
+    ws = L.empty_workspace(dev["desc"], wl.d, wl.k)
+    flag = L.FLAG_PER_HEAD_KERNEL
+    assert L.decode_kernel(dev["desc"].with_flags(flag), wl.d, wl.k) == 2
+    out0, idx0 = _decode_with(L, wl, dev, 0, ws)
+    out1, idx1 = _decode_with(L, wl, dev, flag, ws)
+    assert np.array_equal(idx0, idx1)
+    assert H.rel_err_rows(out1, out0).max() < 1e-5
+    res = H.full_parity(wl, x, out1, idx1)
+    H.log(f"  per-head flag {dtype} B={B} Hq={Hq} Hkv={Hkv} S={S}: {res}")
+
+
 # A head and its helper share out the panel stream (default): each streams one
 # half of the passes and the two hand their scores over through the
 # workspace; a half not published in time is scored by the member needing it.
