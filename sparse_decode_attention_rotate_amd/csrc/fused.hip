@@ -442,9 +442,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
   };
   {
     if constexpr (G == 1) {
+      // ---- 0''. the rest of the rotation runs inside the selection: the
+      // partial sums once the threshold group is known (the P loads have
+      // arrived by then), their reduction after the barriers that follow
       KeyRow<NT, KREG> row(sk, S);  // elements past the row: key 0 (select_keys)
-      select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, ssm.whist,
-                            [&](int i) { LOKI_STAMP(g_stamps_fused, 6 + i); });
+      select_keys<NT, KREG>(row, k, sidx, skey, ssm, blo, bscale, ssm.whist, [&](int i) {
+        LOKI_STAMP(g_stamps_fused, 6 + i);
+        if (i == 0) rotate_rest();
+        if (i == 1) reduce_rest();
+      });
+      __syncthreads();
     } else {
       for (int h = 0; h < G; h++) {
         float l0 = rng[0][0][h], h0 = rng[1][0][h];
@@ -459,12 +466,12 @@ __global__ __launch_bounds__(NT, NT == 256 ? 3 : 2) void fused_kernel(FusedParam
                                      h0);
         __syncthreads();
       }
+      // ---- 0''. finish the rotation: qs[h][DP:D]
+      rotate_rest();
+      __syncthreads();
+      reduce_rest();
+      __syncthreads();
     }
-    // ---- 0''. finish the rotation: qs[h][DP:D]
-    rotate_rest();
-    __syncthreads();
-    reduce_rest();
-    __syncthreads();
   }
 
   LOKI_STAMP(g_stamps_fused, 3);
