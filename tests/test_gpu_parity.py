@@ -653,13 +653,26 @@ def test_decode_append_head_dim_96(L, dtype, separate):
     _decode_append_check(L, wl, separate, selected=True)
 
 
-def test_decode_append_grouped_heads(L):
-    """An appending step of grouped heads on the separate path (g = 4, S above
-    the one-launch limit), with a new key certain to be selected."""
+@pytest.mark.parametrize("separate", [False, True], ids=["default", "separate"])
+def test_decode_append_grouped_heads(L, separate):
+    """An appending step of grouped heads (g = 4, S above the limit of the
+    one-workgroup-per-(b, kv) kernel: the per-head kernel by default), with a
+    new key certain to be selected."""
     wl = _small("bf16", B=2, Hq=8, Hkv=2, S=4500, S_cap=4600, k=600, append=True,
                 heavy_frac=0.02)
-    H.log("decode_append grouped heads")
-    _decode_append_check(L, wl, False, selected=True)
+    H.log(f"decode_append grouped heads separate={separate}")
+    _decode_append_check(L, wl, separate, selected=True)
+
+
+def test_decode_append_grouped_heads_wide_tiles(L):
+    """The separate path's appending step with grouped heads in its widest
+    score tiles: g = 4 and 128 (b, kv) units of 8195 tokens give 2048-token
+    tiles of the rotating score kernel (S * units / 1024 above 1024 tokens),
+    four whole tiles and a 3-token tail (S not a multiple of 4), and the
+    new key certain to be selected."""
+    wl = _small("bf16", B=16, Hq=32, Hkv=8, S=8195, S_cap=8200, k=800, append=True)
+    H.log("decode_append grouped heads, 2048-token score tiles (separate)")
+    _decode_append_check(L, wl, True, selected=True)
 
 
 # One-launch appends: the new token's score enters the selection in the first
