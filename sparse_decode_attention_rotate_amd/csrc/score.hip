@@ -428,13 +428,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_generic_kernel(ScoreParam
 
 // Tokens per tile of the panel kernel with LPT lanes per token: up to 4096
 // (256 KB of an fp16 panel), smaller when that leaves fewer than two
-// workgroups per compute unit (four when a tile also writes the scores of
-// several heads); multiples of two batches; staged tiles hold all g heads'
-// scores of the tile in LDS.
+// workgroups per compute unit (when a tile also writes the scores of several
+// heads: four for groups of four heads, whose 2048-token tiles were measured
+// faster that way, eight for the other group sizes); multiples of two
+// batches; staged tiles hold all g heads' scores of the tile in LDS.
 int tile_tokens(const Shape& sh, int lpt) {
   const int step = (kScoreThreads / lpt) * 2 * kScoreBatch;
   const long long units = (long long)sh.B * sh.Hkv;
-  long long want = (long long)sh.S * units / (sh.g > 1 ? 1024 : 512);
+  const int per_grid = sh.g == 1 ? 512 : (sh.g == 4 ? 1024 : 2048);
+  long long want = (long long)sh.S * units / per_grid;
   const bool staged = lpt == 4 && (sh.g == 1 || sh.g == 2 || sh.g == 4);
   const long long cap = staged ? stage_scores(sh.g) / sh.g : 4096;
   want = want < step ? step : (want > cap ? cap : want);
