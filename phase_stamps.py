@@ -129,6 +129,18 @@ def main():
     for tt in np.arange(0, ts[:, -1].max() + 5, 5.0):
         ph = [int(((ts[:, i] <= tt) & (ts[:, i + 1] > tt)).sum()) for i in range(len(names))]
         lines.append(f"   t={tt:6.1f} " + " ".join(f"{nm}:{c:4d}" for nm, c in zip(names, ph)))
+    # by dispatch round (blocks of 256 workgroups, one per compute unit):
+    # when each round's workgroups finish their phases
+    blk = np.nonzero(used)[0]
+    if len(blk) > 256:
+        lines.append("  by dispatch round (blocks of 256 workgroups): p50 / max end of each phase")
+        for r0 in range(0, blk.max() + 1, 256):
+            m = (blk >= r0) & (blk < r0 + 256)
+            if not m.any():
+                continue
+            cells = " ".join(f"{nm}: {np.median(ts[m, i + 1]):6.2f}/{ts[m, i + 1].max():6.2f}"
+                             for i, nm in enumerate(names))
+            lines.append(f"   blocks {r0:4d}-{min(r0 + 255, blk.max()):4d}  {cells}")
     extra = s[used][:, nb:SLOTS - 1]
     for j in range(extra.shape[1]):
         if (extra[:, j] > 0).all():
