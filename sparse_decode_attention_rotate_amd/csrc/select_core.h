@@ -13,15 +13,14 @@
 //     of 2048 bins (few atomic collisions on spread data) and a DPP prefix
 //     scan over the bins in descending order give the bin b* that holds the
 //     k-th largest score.  lo and scale come from the row's range or, in the
-//     fused kernel, from a first batch of scores (the histogram is then built
-//     while scoring; clamping keeps the binning monotone).
+//     one-launch kernels, from a first batch of scores (the histogram is then
+//     built while scoring; clamping keeps the binning monotone).
 //  2. The last taken element.  Elements are ordered by (order-preserving key
 //     descending, index ascending); the k-th one, (T, I), is found inside b*:
 //     with few members (the common case) one pass over the row collects them
 //     and counts, per wave, the members of higher bins, then a candidate's
 //     rank is one ballot over all candidates (the waves take the candidates
-//     in turn; the fused kernel's select_rows ranks its few in one wave);
-//     otherwise radix passes over 8-bit digits
+//     in turn); otherwise radix passes over 8-bit digits
 //     of the members' keys (per-wave LDS histograms), then the position of the
 //     last taken key among equal keys, then a counting pass.
 //  3. Ordered compaction: element i is taken iff key > T or (key == T and
@@ -82,7 +81,7 @@ __host__ __device__ __forceinline__ float bin_scale(float lo, float hi) {
 }
 
 // LDS scratch of one selection, with the radix passes' per-wave histograms
-// (whist) right after the bin histogram (select_rows keeps its lists in both).
+// (whist) right after the bin histogram.
 template <int NW>
 struct SelectSmem {
   unsigned hist[kBins];
@@ -709,153 +708,6 @@ __device__ __forceinline__ void select_keys(Row& row, int k, int32_t* out_idx, u
                                             SM& sm, float lo, float scale,
                                             unsigned (*whist)[256]) {
   select_keys<NT, KREG>(row, k, out_idx, out_key, sm, lo, scale, whist, [](int) {});
-}
-
-// Entries of each wave's list in select_rows: the lists fill sm.hist and
-// sm.whist, which lie back to back (the scan is done with the first, the
-// radix passes start on the second only after the lists are copied out).
-template <int NT>
-constexpr int kRowListCap = kBins / (NT / 64) + 256;
-
-// Selection for a caller that attends over the selected rows right away.
-// Rows [0, sel_gt) are the members of the bins above b*, in index order: one
-// pass appends them to per-wave lists kept in sm.hist / sm.whist (the scan
-// no longer needs them) while it collects b*'s members; rows [sel_gt, k) are
-// the taken members of b*, also in index order.  mid() runs between that
-// pass and the barrier after it.  Writes rows_idx / rows_val (score, -0 as
-// +0) [0, k) and sm.sel_gt; the caller needs a barrier before reading them.
-// Requires that no wave's list outgrows kRowListCap<NT>: a list holds fewer
-// than k entries and at most a wave's share of the row (KREG * 64), so
-// k - 1 <= kRowListCap<NT> or KREG * 64 <= kRowListCap<NT> suffices.
-template <int NT, int KREG, typename Load, typename Mid>
-__device__ __forceinline__ void select_rows(RowView<NT, KREG, Load>& row, int k, int32_t* rows_idx,
-                                            float* rows_val, SelectSmem<NT / 64>& sm, float lo,
-                                            float scale, Mid&& mid) {
-  constexpr int NW = NT / 64;
-  constexpr int CAP = kRowListCap<NT>;  // >= the length of any wave's list
-  static_assert(sizeof(SelectSmem<NW>::hist) + sizeof(SelectSmem<NW>::whist) >=
-                    sizeof(int) * (size_t)NW * CAP, "lists fit hist and whist");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = row.S;
-
-  select_scan<NT>(sm, k);
-  const int bstar = sm.sel_bin, sel_gt = sm.sel_gt, rem = k - sel_gt, nb = sm.sel_eq;
-  const bool few = nb <= kFewCandidates;
-  int* lists = reinterpret_cast<int*>(sm.hist);
-
-  int cnt = 0;
-  row.each([&](int i, unsigned key) {
-    const int bn = lin_bin(key_score(key), lo, scale);
-    const bool valid = i < S;
-    const bool sure = valid && bn > bstar;
-    const unsigned long long bs = __ballot(sure);
-    if (sure) lists[wave * CAP + cnt + lane_rank(bs)] = i;
-    cnt += __popcll(bs);
-    const bool cand = few && valid && bn == bstar;
-    if (__ballot(cand) != 0ull) {  // rare: this wave row holds members of b*
-      if (cand) {
-        const int slot = atomicAdd(&sm.n_cand, 1);
-        sm.cand_key[slot] = key;
-        sm.cand_idx[slot] = i;
-      }
-    }
-  });
-  if (lane == 0) sm.wcnt[wave] = cnt;
-  mid();
-  __syncthreads();
-
-  // rows [0, sel_gt): the per-wave lists back to back
-  int pre[NW];
-  pre[0] = 0;
-#pragma unroll
-  for (int w = 1; w < NW; w++) pre[w] = pre[w - 1] + sm.wcnt[w - 1];
-  for (int r = tid; r < sel_gt; r += NT) {
-    int w = 0;
-#pragma unroll
-    for (int v = 1; v < NW; v++) w += r >= pre[v] ? 1 : 0;
-    const int i = lists[w * CAP + r - pre[w]];
-    rows_idx[r] = i;
-    rows_val[r] = key_score(order_key(row.load_score(i)));
-  }
-
-  // rows [sel_gt, k): the taken members of b*
-  if (few) {
-    if (wave == 0) {
-      // candidate m on lane m; rank = members ordered before it by
-      // (key descending, index ascending); the rem first are taken
-      const bool mine = lane < nb;
-      const unsigned mk = mine ? sm.cand_key[lane] : 0u;
-      const int mi = mine ? sm.cand_idx[lane] : INT_MAX;
-      int rank = 0;
-      for (int m = 0; m < nb; m++) {
-        const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, m);
-        const int oi = __builtin_amdgcn_readlane(mi, m);
-        rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
-      }
-      const bool taken = mine && rank < rem;
-      int pos = 0;  // among the taken, by index
-      for (int m = 0; m < nb; m++) {
-        const int orank = __builtin_amdgcn_readlane(rank, m);
-        const int oi = __builtin_amdgcn_readlane(mi, m);
-        pos += (orank < rem && oi < mi) ? 1 : 0;
-      }
-      if (taken) {
-        rows_idx[sel_gt + pos] = mi;
-        rows_val[sel_gt + pos] = key_score(mk);
-      }
-    }
-  } else {
-    __syncthreads();  // every list entry is copied out before whist is reused
-    radix_threshold<NT, KREG>(row, bstar, rem, lo, scale, sm, sm.whist);
-    const unsigned T = sm.thr_key;
-    const int I = sm.thr_idx;
-    auto taken = [&](int i, unsigned key) -> bool {
-      return i < S && lin_bin(key_score(key), lo, scale) == bstar &&
-             (key > T || (key == T && i <= I));
-    };
-    int c2 = 0;
-    row.each([&](int i, unsigned key) { c2 += __popcll(__ballot(taken(i, key))); });
-    if (lane == 0) sm.wcnt[wave] = c2;
-    __syncthreads();
-    int out = sel_gt;
-    for (int w = 0; w < wave; w++) out += sm.wcnt[w];
-    row.each([&](int i, unsigned key) {
-      const bool t = taken(i, key);
-      const unsigned long long bt = __ballot(t);
-      const int pos = out + lane_rank(bt);
-      if (t && pos < k) {
-        rows_idx[pos] = i;
-        rows_val[pos] = key_score(key);
-      }
-      out += __popcll(bt);
-    });
-  }
-}
-
-// The rows of select_rows in ascending index order, to global memory: the two
-// index-ordered parts [0, n1) (the members of bins above b*) and [n1, k) (the
-// taken members of b*, usually few) merged: a row of the first part moves up
-// by the taken members below it, a taken member by the first-part rows below
-// it (binary search).  All NT threads, after the rows are visible.
-__device__ __forceinline__ void write_rows_in_index_order(const int32_t* rows, int n1, int k,
-                                                          int32_t* out, int NT) {
-  const int n2 = k - n1;
-  for (int r = threadIdx.x; r < k; r += NT) {
-    const int t = rows[r];
-    int pos;
-    if (r < n1) {
-      pos = r;
-      for (int j = 0; j < n2; j++) pos += rows[n1 + j] < t ? 1 : 0;  // broadcast reads
-    } else {
-      int lo = 0, hi = n1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (rows[mid] < t) lo = mid + 1; else hi = mid;
-      }
-      pos = (r - n1) + lo;
-    }
-    out[pos] = t;
-  }
 }
 
 // Rows of more than 16384 scores (32 order keys per thread, or re-read
