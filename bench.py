@@ -727,6 +727,12 @@ def time_workload(name, args, headline=None):
         alg = nominal_bytes
         entry["alg_bytes"] = alg
     gbs = alg / (us * 1e-6) / 1e9
+    # HBM bytes per launch of the step's one-launch kernel from the committed
+    # counter record of this workload, while it matches the kernel's source
+    kern = PLAN_KERNEL.get(code)
+    trec = measured_traffic(wl.name, kern) if kern else None
+    entry["traffic"] = trec.get("hbm_bytes_per_launch") if trec else None
+    entry["traffic_over_alg"] = round(entry["traffic"] / alg, 4) if entry["traffic"] else None
     entry.update({"GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                   "target_us_at_70pct": round(alg / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6, 2),
                   "dense_attention_us": round(dense_us, 2),
