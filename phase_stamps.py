@@ -141,6 +141,28 @@ def main():
             cells = " ".join(f"{nm}: {np.median(ts[m, i + 1]):6.2f}/{ts[m, i + 1].max():6.2f}"
                              for i, nm in enumerate(names))
             lines.append(f"   blocks {r0:4d}-{min(r0 + 255, blk.max()):4d}  {cells}")
+    # compute units: HW_ID (last slot) gives CU_ID [11:8], SH_ID [12],
+    # SE_ID [15:13]; workgroup i runs on XCD i % 8
+    hw = s[:, SLOTS - 1]
+    cu = ((blk % 8) << 16) | (((hw[blk] >> 13) & 7) << 8) | (((hw[blk] >> 12) & 1) << 4) | \
+        ((hw[blk] >> 8) & 15)
+    ucu, cnt = np.unique(cu, return_counts=True)
+    lines.append(f"  compute units used: {len(ucu)}; workgroups per compute unit: "
+                 + ", ".join(f"{c} on {n}" for c, n in zip(*np.unique(cnt, return_counts=True))))
+    if len(blk) > 256:
+        same = np.mean([cu[i] == cu[i + 256] for i in range(len(blk) - 256)
+                        if blk[i] + 256 == blk[i + 256]])
+        lines.append(f"  workgroups w and w + 256 on one compute unit: {same:.2f} of the pairs")
+        # on compute units holding two workgroups: the later-dispatched one's
+        # stream end against the earlier one's
+        first, second = [], []
+        for c in ucu[cnt == 2]:
+            w = np.sort(np.nonzero(cu == c)[0])
+            first.append(ts[w[0], 2])
+            second.append(ts[w[1], 2])
+        if first:
+            lines.append(f"  two per compute unit: scores end p50 {np.median(first):.2f} (first "
+                         f"dispatched) / {np.median(second):.2f} (second)")
     extra = s[used][:, nb:SLOTS - 1]
     for j in range(extra.shape[1]):
         if (extra[:, j] > 0).all():
