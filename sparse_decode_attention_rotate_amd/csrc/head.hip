@@ -22,7 +22,9 @@
 //     ascending order, and their low-dim partial logits (the index set, when
 //     asked for, is a copy of that list);
 //  3. block_attend (attend_core.h) gathers the selected key tails and value
-//     rows.
+//     rows: with the nontemporal policy for a single query head per KV head,
+//     with the default one for grouped heads, whose siblings on the same XCD
+//     select some of the same rows.
 // Grouped query heads: the g heads of one (b, kv) are g workgroups on one XCD
 // (workgroup i runs on XCD i % 8), each streaming the same panel with the
 // default cache policy, so that the panel comes from HBM once and from that
@@ -532,8 +534,14 @@ __global__ __launch_bounds__(NT, 4) void head_kernel(HeadParams p) {
   const int r0 = paired && helper ? p.k0 : 0;
   const int nr = paired ? (helper ? k - p.k0 : p.k0) : k;
   float M, Lsum, A;
-  block_attend<DT, D, NT, true, kHeadRowsPerBatch, false, true>(
-      qs, p.scale_log2, sidx + r0, skey + r0, nr, p.kcache, p.vcache, head, sh, asm_, M, Lsum, A);
+  if (sh.g > 1)  // grouped heads: rows selected by several heads of a group come from L2
+    block_attend<DT, D, NT, true, kHeadRowsPerBatch, false, false>(
+        qs, p.scale_log2, sidx + r0, skey + r0, nr, p.kcache, p.vcache, head, sh, asm_, M, Lsum,
+        A);
+  else
+    block_attend<DT, D, NT, true, kHeadRowsPerBatch, false, true>(
+        qs, p.scale_log2, sidx + r0, skey + r0, nr, p.kcache, p.vcache, head, sh, asm_, M, Lsum,
+        A);
   if (paired) {
     // owner: rows [0, k0); helper: rows [k0, k).  Partials (M, L, A[D]) of
     // pair j: owner's at help_part[2j], helper's at help_part[2j+1].
